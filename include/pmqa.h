@@ -1,0 +1,181 @@
+/*
+ * pmqa.h - C ABI of the MI355X (gfx950) paged MQA logits library.
+ *
+ * The operation is the scoring step of a DeepSeek-style sparse-attention
+ * indexer described on the page "[flashinfer] Blackwell 아키텍처를 위한
+ * 고성능 Paged MQA Logits 커널 도입" (introduction: the indexer selects KV
+ * tokens from a per-head weighted sum of rectified scores; an fp8 and an fp4
+ * kernel).  For output row r (query j of batch row b, r = b*next_n + j) and
+ * KV token t reached through the block table:
+ *
+ *     logits[r, t] = sum_h w[r, h] * ReLU(scale_t * dot(q[r, h, :], k_t))
+ *                                        for t <  ctx_b - next_n + 1 + j
+ *     logits[r, t] = -inf                for the other t < max_context_len
+ *
+ * Work is cut into 256-token units of one batch row and spread over a
+ * persistent grid by a schedule computed on the GPU (sections 1 and 2 of the
+ * same page: binary search over per-row unit counts, zero-length rows
+ * skipped, no host round trip so the pair of calls can be graph-captured).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers are DEVICE pointers unless stated otherwise.  Every buffer is
+ *    owned by the caller; the library never allocates, frees or retains one.
+ *  - Calls are asynchronous on `stream` and never synchronize the host,
+ *    except in validate mode (below).  No call allocates device memory, so
+ *    compute_schedule followed by a logits call can be captured into a HIP
+ *    graph and replayed.
+ *  - No C++ exception crosses the ABI.  Every call returns a pmqa_status_t;
+ *    pmqa_last_error() returns a message naming the offending argument.
+ *  - Always-on checks cost O(1) host work: null pointers, alignment, sizes,
+ *    strides, the compiled specialisation (num_heads 64, head_dim 128,
+ *    page_size 64, next_n 1 or 2) and, once per device, that the device is a
+ *    gfx950.
+ *  - Validate mode (environment variable PMQA_VALIDATE_INPUTS=1, read on
+ *    every call) adds checks of device contents: context lengths, the used
+ *    block-table entries and the schedule's freshness.  They copy data to the
+ *    host and synchronize `stream`, so validate mode refuses a capturing
+ *    stream with PMQA_ERR_CAPTURING.
+ *  - Without validate mode, out-of-range device contents never make the
+ *    kernels read or write outside the buffers described here (indices are
+ *    clamped), but the results are then unspecified.
+ */
+#ifndef PMQA_H
+#define PMQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compiled specialisation. */
+#define PMQA_NUM_HEADS 64
+#define PMQA_HEAD_DIM 128
+#define PMQA_PAGE_SIZE 64
+#define PMQA_UNIT_TOKENS 256 /* one schedule work unit = 4 pages of one row */
+#define PMQA_FP8_PAGE_BYTES 8448 /* 64*128 e4m3fn + 64 fp32 scales */
+#define PMQA_FP4_PAGE_BYTES 4352 /* 64*64 packed e2m1 + 64*4 e8m0 */
+
+typedef enum {
+  PMQA_OK = 0,
+  PMQA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or stride */
+  PMQA_ERR_UNSUPPORTED = 2,      /* not a gfx950 device, or shape not compiled */
+  PMQA_ERR_INVALID_VALUE = 3,    /* validate mode: bad context length or page id */
+  PMQA_ERR_STALE_SCHEDULE = 4,   /* validate mode: schedule does not match inputs */
+  PMQA_ERR_CAPTURING = 5,        /* validate mode on a capturing stream */
+  PMQA_ERR_HIP = 6               /* a HIP runtime call failed */
+} pmqa_status_t;
+
+typedef enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_FP4 = 1 } pmqa_variant_t;
+
+/* Message of the last failing call on this thread ("" after success).  The
+ * string is owned by the library and valid until the next call on the
+ * thread. */
+const char* pmqa_last_error(void);
+
+/* Persistent-grid size for a logits kernel on `device`: compute units times
+ * the kernel's resident workgroups per compute unit times 4 wavefronts per
+ * workgroup (one worker = one wavefront).  Host-only query; writes the count
+ * to *num_workers (host pointer). */
+pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next_n,
+                                       int32_t* num_workers);
+
+/* Bytes of a schedule buffer for `batch` rows and `num_workers` workers:
+ * 4 * (8 + 2*(num_workers+1) + batch + 1).  Returns 0 for invalid sizes. */
+size_t pmqa_schedule_bytes(int32_t batch, int32_t num_workers);
+
+/*
+ * compute_schedule - per-call persistent-worker partition, on the GPU.
+ *
+ * Page: sections 1-2 (linear partition scan replaced by a binary search;
+ * schedule computed on the GPU so it can be graph-captured) and the general
+ * lessons (a schedule stays valid only while every ceil(context_len/256) is
+ * unchanged).
+ *
+ *   context_lens  int32 [batch]; lengths < 0 count as 0 units.
+ *   batch         >= 1.
+ *   num_workers   >= 1; must equal the value later passed to the logits call.
+ *   schedule      int32 buffer of pmqa_schedule_bytes(batch, num_workers)
+ *                 bytes, 4-byte aligned, written entirely:
+ *     [0] magic 0x41514D50, [1] batch, [2] num_workers, [3] total units T
+ *         (-1 if T would exceed 2^31-1; the logits calls then write only
+ *         -inf), [4] unit tokens (256), [5..7] zero;
+ *     [8 + 2w], [9 + 2w]  start (row, unit) of worker w, w = 0..num_workers;
+ *         worker w owns global units [floor(w*T/W), floor((w+1)*T/W)) of the
+ *         row-major sequence of (row, unit) pairs; a start never names a row
+ *         with zero units; worker num_workers starts at (batch, 0);
+ *     [10 + 2*num_workers + b]  exclusive prefix sum S[b] of
+ *         c_b = ceil(context_lens[b]/256), b = 0..batch.
+ *
+ * One workgroup; no host synchronization.
+ */
+pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                               int32_t* schedule, hipStream_t stream);
+
+/*
+ * paged_mqa_logits_fp8 - logits from an fp8 paged K cache.
+ *
+ * Page: introduction (fp8 kernel, weighted sum of rectified scores) and
+ * section 1 (zero-length rows skipped by the task iterator).
+ *
+ *   q             e4m3fn [batch, next_n, 64, 128], contiguous, 16-B aligned.
+ *   kv_cache      uint8 [num_pages][8448], 16-B aligned: per page 64 tokens x
+ *                 128 e4m3fn bytes (token-major), then 64 little-endian fp32
+ *                 per-token scales.  Only pages of tokens t < ctx_b are read.
+ *   weights       fp32 [batch*next_n, 64], contiguous, 16-B aligned.
+ *   context_lens  int32 [batch].
+ *   block_table   int32 [batch, block_table_stride]; entry i of row b names
+ *                 the physical page of tokens [64i, 64i+64).  Only entries
+ *                 i < ceil(ctx_b/64) are read.
+ *   schedule      from compute_schedule(context_lens, batch, num_workers).
+ *   logits        fp32 [batch*next_n, logits_stride], 16-B aligned,
+ *                 logits_stride % 4 == 0 and >= max_context_len.  Row
+ *                 r = b*next_n + j gets columns [0, max_context_len): the
+ *                 scores for t < min(ctx_b - next_n + 1 + j, max_context_len)
+ *                 and -inf for the rest (tokens >= max_context_len are
+ *                 truncated).  Columns >= max_context_len are not touched.
+ *   num_heads 64, head_dim 128, page_size 64, next_n 1 or 2 (else
+ *   PMQA_ERR_UNSUPPORTED); num_pages >= 1; block_table_stride >= 1;
+ *   max_context_len >= 1.
+ */
+pmqa_status_t paged_mqa_logits_fp8(const void* q, const void* kv_cache, const float* weights,
+                                   const int32_t* context_lens, const int32_t* block_table,
+                                   const int32_t* schedule, float* logits, int32_t batch,
+                                   int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                   int32_t page_size, int64_t num_pages,
+                                   int32_t block_table_stride, int32_t max_context_len,
+                                   int64_t logits_stride, int32_t num_workers,
+                                   hipStream_t stream);
+
+/*
+ * paged_mqa_logits_fp4 - logits from an MXFP4 paged K cache.
+ *
+ * Page: introduction (fp4 kernel).  Elements are OCP MXFP4: E2M1 values with
+ * one E8M0 scale per 32 consecutive elements along head_dim; there is no
+ * per-token fp32 scale (scale_t = 1).
+ *
+ *   q             packed e2m1 [batch, next_n, 64, 64] (element 2i in the low
+ *                 nibble of byte i), 16-B aligned.
+ *   q_scale       e8m0 [batch, next_n, 64, 4] (no alignment requirement).
+ *   kv_cache      uint8 [num_pages][4352], 16-B aligned: 64 tokens x 64 packed
+ *                 bytes (token-major), then 64 tokens x 4 e8m0 block scales.
+ *   All other arguments as for paged_mqa_logits_fp8.
+ */
+pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const void* kv_cache,
+                                   const float* weights, const int32_t* context_lens,
+                                   const int32_t* block_table, const int32_t* schedule,
+                                   float* logits, int32_t batch, int32_t next_n,
+                                   int32_t num_heads, int32_t head_dim, int32_t page_size,
+                                   int64_t num_pages, int32_t block_table_stride,
+                                   int32_t max_context_len, int64_t logits_stride,
+                                   int32_t num_workers, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMQA_H */

@@ -1,0 +1,225 @@
+"""Python binding of the MI355X paged MQA logits library (``libpmqa.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/pmqa.h``.  torch provides
+device memory and the current stream; tensors are passed as raw pointers.
+There is no fallback: importing this package fails if the library has not
+been built (``python -m paged_mqa_logits_amd.build``).
+
+Entry points (same names as the C ABI):
+
+    compute_schedule(context_lens, num_workers=None, out=None) -> schedule
+    paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table,
+                         schedule, max_context_len, out=None) -> logits
+    paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
+                         block_table, schedule, max_context_len, out=None)
+    default_num_workers(variant, next_n=1, device=None)
+    schedule_bytes(batch, num_workers)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpmqa.so")
+
+NUM_HEADS = 64
+HEAD_DIM = 128
+PAGE_SIZE = 64
+UNIT_TOKENS = 256
+FP8_PAGE_BYTES = 8448
+FP4_PAGE_BYTES = 4352
+SCHED_HEADER = 8
+SCHED_MAGIC = 0x41514D50
+
+VARIANT_FP8 = 0
+VARIANT_FP4 = 1
+
+STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED",
+          3: "PMQA_ERR_INVALID_VALUE", 4: "PMQA_ERR_STALE_SCHEDULE",
+          5: "PMQA_ERR_CAPTURING", 6: "PMQA_ERR_HIP"}
+
+EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
+           "compute_schedule", "paged_mqa_logits_fp8", "paged_mqa_logits_fp4")
+
+
+class PmqaError(RuntimeError):
+    """A library call returned a status other than PMQA_OK."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m paged_mqa_logits_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+_lib.pmqa_last_error.restype = ctypes.c_char_p
+_lib.pmqa_last_error.argtypes = []
+_lib.pmqa_schedule_bytes.restype = ctypes.c_size_t
+_lib.pmqa_schedule_bytes.argtypes = [_i32, _i32]
+_lib.pmqa_default_num_workers.restype = ctypes.c_int
+_lib.pmqa_default_num_workers.argtypes = [ctypes.c_int, _i32, _i32, ctypes.POINTER(_i32)]
+_lib.compute_schedule.restype = ctypes.c_int
+_lib.compute_schedule.argtypes = [_p, _i32, _i32, _p, _p]
+_lib.paged_mqa_logits_fp8.restype = ctypes.c_int
+_lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                      _i64, _i32, _i32, _i64, _i32, _p]
+_lib.paged_mqa_logits_fp4.restype = ctypes.c_int
+_lib.paged_mqa_logits_fp4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                      _i32, _i64, _i32, _i32, _i64, _i32, _p]
+
+
+def library():
+    """The loaded ctypes library (for tests of the raw ABI)."""
+    return _lib
+
+
+def last_error():
+    return _lib.pmqa_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise PmqaError(status, last_error())
+
+
+def _stream_ptr(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtypes, ndim=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BYTE = (torch.uint8, torch.float8_e4m3fn, torch.int8)
+
+
+def schedule_bytes(batch, num_workers):
+    return int(_lib.pmqa_schedule_bytes(int(batch), int(num_workers)))
+
+
+def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None):
+    dev = torch.cuda.current_device() if device is None else int(device)
+    out = _i32(0)
+    _check(_lib.pmqa_default_num_workers(dev, int(variant), int(next_n), ctypes.byref(out)))
+    return int(out.value)
+
+
+def compute_schedule(context_lens, num_workers=None, out=None, variant=VARIANT_FP8, next_n=1,
+                     stream=None):
+    """Schedule (int32 tensor) of the persistent workers for these lengths."""
+    _need(context_lens, "context_lens", (torch.int32,), ndim=1)
+    B = context_lens.shape[0]
+    W = default_num_workers(variant, next_n) if num_workers is None else int(num_workers)
+    words = schedule_bytes(B, W) // 4
+    if out is None:
+        out = torch.empty(words, dtype=torch.int32, device=context_lens.device)
+    else:
+        _need(out, "out", (torch.int32,))
+        if out.numel() < words:
+            raise ValueError(f"schedule buffer has {out.numel()} words, needs {words}")
+    _check(_lib.compute_schedule(_ptr(context_lens), B, W, _ptr(out), _stream_ptr(stream)))
+    return out
+
+
+def schedule_workers(schedule):
+    """num_workers recorded in a schedule tensor's header (reads the device)."""
+    return int(schedule[2].item())
+
+
+def _logits_out(out, rows, max_context_len, device):
+    if out is None:
+        ldo = (max_context_len + 3) // 4 * 4
+        buf = torch.empty((rows, ldo), dtype=torch.float32, device=device)
+        return buf[:, :max_context_len], ldo, buf
+    _need(out, "out", (torch.float32,), ndim=2, contiguous=False)
+    if out.shape[0] != rows or out.shape[1] < max_context_len or out.stride(1) != 1:
+        raise ValueError(f"out must be [{rows}, >= {max_context_len}] with unit column stride")
+    return out, out.stride(0), out
+
+
+def paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table, schedule,
+                         max_context_len, out=None, num_workers=None, stream=None):
+    """fp8 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+    _need(q, "q", _BYTE, ndim=4)
+    _need(kv_cache, "kv_cache", _BYTE, ndim=2)
+    _need(weights, "weights", (torch.float32,), ndim=2)
+    _need(context_lens, "context_lens", (torch.int32,), ndim=1)
+    _need(block_table, "block_table", (torch.int32,), ndim=2)
+    _need(schedule, "schedule", (torch.int32,), ndim=1)
+    B, NN, H, D = q.shape
+    if kv_cache.shape[1] != FP8_PAGE_BYTES:
+        raise ValueError(f"kv_cache rows must be {FP8_PAGE_BYTES} bytes, got {kv_cache.shape[1]}")
+    if tuple(weights.shape) != (B * NN, H):
+        raise ValueError(f"weights must be [{B * NN}, {H}], got {tuple(weights.shape)}")
+    if context_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("context_lens and block_table must have one row per batch row")
+    W = _sched_workers(schedule, B, num_workers)
+    view, ldo, buf = _logits_out(out, B * NN, int(max_context_len), q.device)
+    _check(_lib.paged_mqa_logits_fp8(
+        _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
+        _ptr(schedule), _ptr(buf), B, NN, H, D, PAGE_SIZE, kv_cache.shape[0],
+        block_table.shape[1], int(max_context_len), ldo, W, _stream_ptr(stream)))
+    return view
+
+
+def paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_table, schedule,
+                         max_context_len, out=None, num_workers=None, stream=None):
+    """MXFP4 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+    _need(q, "q", _BYTE, ndim=4)
+    _need(q_scale, "q_scale", (torch.uint8, torch.float8_e8m0fnu), ndim=4)
+    _need(kv_cache, "kv_cache", _BYTE, ndim=2)
+    _need(weights, "weights", (torch.float32,), ndim=2)
+    _need(context_lens, "context_lens", (torch.int32,), ndim=1)
+    _need(block_table, "block_table", (torch.int32,), ndim=2)
+    _need(schedule, "schedule", (torch.int32,), ndim=1)
+    B, NN, H, Dh = q.shape
+    if tuple(q_scale.shape) != (B, NN, H, 2 * Dh // 32):
+        raise ValueError(f"q_scale must be [{B}, {NN}, {H}, {2 * Dh // 32}]")
+    if kv_cache.shape[1] != FP4_PAGE_BYTES:
+        raise ValueError(f"kv_cache rows must be {FP4_PAGE_BYTES} bytes, got {kv_cache.shape[1]}")
+    if tuple(weights.shape) != (B * NN, H):
+        raise ValueError(f"weights must be [{B * NN}, {H}], got {tuple(weights.shape)}")
+    if context_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("context_lens and block_table must have one row per batch row")
+    W = _sched_workers(schedule, B, num_workers)
+    view, ldo, buf = _logits_out(out, B * NN, int(max_context_len), q.device)
+    _check(_lib.paged_mqa_logits_fp4(
+        _ptr(q), _ptr(q_scale), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
+        _ptr(block_table), _ptr(schedule), _ptr(buf), B, NN, H, 2 * Dh, PAGE_SIZE,
+        kv_cache.shape[0], block_table.shape[1], int(max_context_len), ldo, W,
+        _stream_ptr(stream)))
+    return view
+
+
+def _sched_workers(schedule, batch, num_workers):
+    """Worker count implied by the schedule's length (no device read)."""
+    if num_workers is not None:
+        return int(num_workers)
+    words = schedule.numel()
+    w2 = words - SCHED_HEADER - 2 - batch - 1        # = 2 * num_workers
+    if w2 < 2 or w2 % 2:
+        raise ValueError(f"schedule of {words} words does not fit batch {batch}; "
+                         "pass num_workers explicitly")
+    return w2 // 2

@@ -1,0 +1,295 @@
+// C-ABI entry points of the paged MQA logits library (declared in pmqa.h).
+//
+// Argument checks follow the page "[flashinfer] Blackwell 아키텍처를 위한 고성능
+// Paged MQA Logits 커널 도입" (why-it-matters section and reviewer feedback:
+// optional input validation at the API boundary; the schedule must be
+// recomputed whenever a context length crosses a 256-token boundary).  Every
+// check that needs only host data is always on; checks of device contents
+// run in validate mode (PMQA_VALIDATE_INPUTS=1) because they synchronize.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "../../include/pmqa.h"
+#include "pmqa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pmqa_status_t fail(pmqa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pmqa_status_t ok() {
+  g_err[0] = '\0';
+  return PMQA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch[kMaxDevices];
+
+pmqa_status_t check_device(int* dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PMQA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  int st = g_arch[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(PMQA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return fail(PMQA_ERR_UNSUPPORTED, "device %d is not a gfx950 (MI355X)", dev);
+  if (dev_out) *dev_out = dev;
+  return PMQA_OK;
+}
+
+bool validate_mode() {
+  const char* v = getenv("PMQA_VALIDATE_INPUTS");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t sched_words(int64_t batch, int64_t workers) {
+  return pmqa::kSchedHeader + 2 * (workers + 1) + batch + 1;
+}
+
+struct Shape {
+  int32_t batch, next_n, bt_stride, max_ctx, workers;
+  int64_t num_pages, ldo;
+};
+
+pmqa_status_t check_shape(const Shape& s, int32_t num_heads, int32_t head_dim, int32_t page_size) {
+  if (s.batch < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "batch = %d must be >= 1", s.batch);
+  if (num_heads != pmqa::kHeads || head_dim != pmqa::kHeadDim || page_size != pmqa::kPage)
+    return fail(PMQA_ERR_UNSUPPORTED,
+                "(num_heads, head_dim, page_size) = (%d, %d, %d) not compiled; only (64, 128, 64)",
+                num_heads, head_dim, page_size);
+  if (s.next_n != 1 && s.next_n != 2)
+    return fail(PMQA_ERR_UNSUPPORTED, "next_n = %d not compiled; only 1 or 2", s.next_n);
+  if (s.num_pages < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_pages = %lld must be >= 1", (long long)s.num_pages);
+  if (s.bt_stride < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "block_table_stride = %d must be >= 1", s.bt_stride);
+  if (s.max_ctx < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "max_context_len = %d must be >= 1", s.max_ctx);
+  if (s.ldo < s.max_ctx)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "logits_stride = %lld < max_context_len = %d",
+                (long long)s.ldo, s.max_ctx);
+  if (s.ldo % 4 != 0)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "logits_stride = %lld must be a multiple of 4",
+                (long long)s.ldo);
+  if (s.workers < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_workers = %d must be >= 1", s.workers);
+  if ((int64_t)s.batch * s.next_n > INT32_MAX / pmqa::kHeads)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "batch*next_n = %lld too large",
+                (long long)s.batch * s.next_n);
+  return PMQA_OK;
+}
+
+// Validate mode: device contents, read back to the host.
+pmqa_status_t validate_contents(const int32_t* ctx, const int32_t* bt, const int32_t* sched,
+                                const Shape& s, hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(PMQA_ERR_CAPTURING, "PMQA_VALIDATE_INPUTS is set but the stream is capturing");
+  std::vector<int32_t> hctx(s.batch);
+  std::vector<int32_t> hbt((size_t)s.batch * s.bt_stride);
+  std::vector<int32_t> hs(sched_words(s.batch, s.workers));
+  e = hipMemcpyAsync(hctx.data(), ctx, hctx.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(hbt.data(), bt, hbt.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(hs.data(), sched, hs.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "validate copy: %s", hipGetErrorString(e));
+  const int32_t* S = hs.data() + pmqa::kSchedHeader + 2 * (s.workers + 1);
+  if (hs[0] != pmqa::kSchedMagic || hs[1] != s.batch || hs[2] != s.workers)
+    return fail(PMQA_ERR_STALE_SCHEDULE,
+                "schedule header (magic %08x, batch %d, workers %d) does not match the call "
+                "(batch %d, workers %d)",
+                (unsigned)hs[0], hs[1], hs[2], s.batch, s.workers);
+  if (hs[3] < 0)
+    return fail(PMQA_ERR_INVALID_VALUE, "total work units exceed 2^31-1");
+  for (int32_t b = 0; b < s.batch; ++b) {
+    const int32_t L = hctx[b];
+    if (L < 0) return fail(PMQA_ERR_INVALID_VALUE, "context_lens[%d] = %d < 0", b, L);
+    const int64_t pages = ((int64_t)L + pmqa::kPage - 1) / pmqa::kPage;
+    if (pages > s.bt_stride)
+      return fail(PMQA_ERR_INVALID_VALUE,
+                  "context_lens[%d] = %d needs %lld pages > block_table_stride %d", b, L,
+                  (long long)pages, s.bt_stride);
+    const int32_t c = (int32_t)(((int64_t)L + pmqa::kUnit - 1) / pmqa::kUnit);
+    if (S[b + 1] - S[b] != c)
+      return fail(PMQA_ERR_STALE_SCHEDULE,
+                  "schedule is stale: row %d has %d units, context_lens[%d] = %d needs %d "
+                  "(recompute the schedule when ceil(context_len/256) changes)",
+                  b, S[b + 1] - S[b], b, L, c);
+    const int64_t used = pages < s.bt_stride ? pages : s.bt_stride;
+    for (int64_t i = 0; i < used; ++i) {
+      const int32_t pid = hbt[(size_t)b * s.bt_stride + i];
+      if (pid < 0 || pid >= s.num_pages)
+        return fail(PMQA_ERR_INVALID_VALUE, "block_table[%d, %lld] = %d outside [0, %lld)", b,
+                    (long long)i, pid, (long long)s.num_pages);
+    }
+  }
+  return PMQA_OK;
+}
+
+pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, const void* kv,
+                            const float* weights, const int32_t* ctx, const int32_t* bt,
+                            const int32_t* sched, float* logits, const Shape& s,
+                            int32_t num_heads, int32_t head_dim, int32_t page_size,
+                            hipStream_t stream) {
+  if (!q) return fail(PMQA_ERR_INVALID_ARGUMENT, "q is null");
+  if (variant == PMQA_VARIANT_FP4 && !q_scale)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "q_scale is null");
+  if (!kv) return fail(PMQA_ERR_INVALID_ARGUMENT, "kv_cache is null");
+  if (!weights) return fail(PMQA_ERR_INVALID_ARGUMENT, "weights is null");
+  if (!ctx) return fail(PMQA_ERR_INVALID_ARGUMENT, "context_lens is null");
+  if (!bt) return fail(PMQA_ERR_INVALID_ARGUMENT, "block_table is null");
+  if (!sched) return fail(PMQA_ERR_INVALID_ARGUMENT, "schedule is null");
+  if (!logits) return fail(PMQA_ERR_INVALID_ARGUMENT, "logits is null");
+  if (!aligned(q, 16)) return fail(PMQA_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
+  if (!aligned(kv, 16)) return fail(PMQA_ERR_INVALID_ARGUMENT, "kv_cache must be 16-byte aligned");
+  if (!aligned(weights, 16))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
+  if (!aligned(logits, 16))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "logits must be 16-byte aligned");
+  if (!aligned(ctx, 4) || !aligned(bt, 4) || !aligned(sched, 4))
+    return fail(PMQA_ERR_INVALID_ARGUMENT,
+                "context_lens, block_table and schedule must be 4-byte aligned");
+  pmqa_status_t st = check_shape(s, num_heads, head_dim, page_size);
+  if (st != PMQA_OK) return st;
+  st = check_device(nullptr);
+  if (st != PMQA_OK) return st;
+  if (validate_mode()) {
+    st = validate_contents(ctx, bt, sched, s, stream);
+    if (st != PMQA_OK) return st;
+  }
+  pmqa::LogitsArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.q_scale = static_cast<const uint8_t*>(q_scale);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.weights = weights;
+  a.ctx = ctx;
+  a.bt = bt;
+  a.sched = sched;
+  a.out = logits;
+  a.num_pages = s.num_pages;
+  a.ldo = s.ldo;
+  a.batch = s.batch;
+  a.bt_stride = s.bt_stride;
+  a.max_ctx = s.max_ctx;
+  a.num_workers = s.workers;
+  const hipError_t e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
+                                                   : pmqa::launch_logits_fp4(a, s.next_n, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pmqa_last_error(void) { return g_err; }
+
+size_t pmqa_schedule_bytes(int32_t batch, int32_t num_workers) {
+  if (batch < 1 || num_workers < 1) return 0;
+  return (size_t)sched_words(batch, num_workers) * sizeof(int32_t);
+}
+
+pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next_n,
+                                       int32_t* num_workers) {
+  if (!num_workers) return fail(PMQA_ERR_INVALID_ARGUMENT, "num_workers is null");
+  if (variant != PMQA_VARIANT_FP8 && variant != PMQA_VARIANT_FP4)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "variant = %d is not fp8 (0) or fp4 (1)", variant);
+  if (next_n != 1 && next_n != 2)
+    return fail(PMQA_ERR_UNSUPPORTED, "next_n = %d not compiled; only 1 or 2", next_n);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (device != cur) {
+    e = hipSetDevice(device);
+    if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
+  }
+  pmqa_status_t st = check_device(nullptr);
+  int cus = 0, blocks = 0;
+  if (st == PMQA_OK) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess) e = pmqa::logits_blocks_per_cu(variant, next_n, &blocks);
+    if (e != hipSuccess) st = fail(PMQA_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  }
+  if (device != cur) hipSetDevice(cur);
+  if (st != PMQA_OK) return st;
+  if (blocks < 1) blocks = 1;
+  *num_workers = cus * blocks * pmqa::kWavesPerBlock;
+  return ok();
+}
+
+pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                               int32_t* schedule, hipStream_t stream) {
+  if (!context_lens) return fail(PMQA_ERR_INVALID_ARGUMENT, "context_lens is null");
+  if (!schedule) return fail(PMQA_ERR_INVALID_ARGUMENT, "schedule is null");
+  if (!aligned(context_lens, 4) || !aligned(schedule, 4))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "context_lens and schedule must be 4-byte aligned");
+  if (batch < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "batch = %d must be >= 1", batch);
+  if (num_workers < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_workers = %d must be >= 1", num_workers);
+  if (sched_words(batch, num_workers) > INT32_MAX)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "batch + 2*num_workers too large");
+  pmqa_status_t st = check_device(nullptr);
+  if (st != PMQA_OK) return st;
+  const hipError_t e = pmqa::launch_schedule(context_lens, batch, num_workers, schedule, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "schedule launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pmqa_status_t paged_mqa_logits_fp8(const void* q, const void* kv_cache, const float* weights,
+                                   const int32_t* context_lens, const int32_t* block_table,
+                                   const int32_t* schedule, float* logits, int32_t batch,
+                                   int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                   int32_t page_size, int64_t num_pages,
+                                   int32_t block_table_stride, int32_t max_context_len,
+                                   int64_t logits_stride, int32_t num_workers,
+                                   hipStream_t stream) {
+  const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
+                logits_stride};
+  return logits_common(PMQA_VARIANT_FP8, q, nullptr, kv_cache, weights, context_lens,
+                       block_table, schedule, logits, s, num_heads, head_dim, page_size, stream);
+}
+
+pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const void* kv_cache,
+                                   const float* weights, const int32_t* context_lens,
+                                   const int32_t* block_table, const int32_t* schedule,
+                                   float* logits, int32_t batch, int32_t next_n,
+                                   int32_t num_heads, int32_t head_dim, int32_t page_size,
+                                   int64_t num_pages, int32_t block_table_stride,
+                                   int32_t max_context_len, int64_t logits_stride,
+                                   int32_t num_workers, hipStream_t stream) {
+  const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
+                logits_stride};
+  return logits_common(PMQA_VARIANT_FP4, q, q_scale, kv_cache, weights, context_lens,
+                       block_table, schedule, logits, s, num_heads, head_dim, page_size, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal host-side declarations shared by the C-ABI layer (api.cpp) and the
+// HIP translation units that own the kernels.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace pmqa {
+
+constexpr int kHeads = 64;
+constexpr int kHeadDim = 128;
+constexpr int kPage = 64;
+constexpr int kUnit = 256;
+constexpr int kPagesPerUnit = kUnit / kPage;
+constexpr int kFp8PageBytes = kPage * kHeadDim + 4 * kPage;       // 8448
+constexpr int kFp4PageBytes = kPage * kHeadDim / 2 + kPage * kHeadDim / 32;  // 4352
+constexpr int kSchedHeader = 8;
+constexpr int32_t kSchedMagic = 0x41514D50;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = 64 * kWavesPerBlock;
+
+// Arguments of one logits launch (passed by value to the kernel).
+struct LogitsArgs {
+  const uint8_t* q;         // fp8: e4m3 [B, NN, H, D]; fp4: packed e2m1 [B, NN, H, D/2]
+  const uint8_t* q_scale;   // fp4 only: e8m0 [B, NN, H, D/32]
+  const uint8_t* kv;        // [num_pages][page bytes]
+  const float* weights;     // [B*NN, H]
+  const int32_t* ctx;       // [B]
+  const int32_t* bt;        // [B, bt_stride]
+  const int32_t* sched;     // compute_schedule output
+  float* out;               // [B*NN, ldo]
+  int64_t num_pages;
+  int64_t ldo;
+  int32_t batch;
+  int32_t bt_stride;
+  int32_t max_ctx;
+  int32_t num_workers;
+};
+
+// Launchers (defined next to their kernels).  Return the launch status.
+hipError_t launch_schedule(const int32_t* ctx, int32_t batch, int32_t num_workers,
+                           int32_t* sched, hipStream_t stream);
+hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, hipStream_t stream);
+hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream);
+
+// Resident workgroups per compute unit of a logits kernel (occupancy query).
+hipError_t logits_blocks_per_cu(int variant, int next_n, int* blocks);
+
+}  // namespace pmqa

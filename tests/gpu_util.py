@@ -1,0 +1,51 @@
+"""Helpers for the GPU tests: upload seeded inputs, call the library through
+its Python binding (which calls the C ABI), and bring results back."""
+import numpy as np
+import torch
+
+import paged_mqa_logits_amd as pmqa
+
+
+def upload(data):
+    dev = {}
+    for k in ("q", "q_scale", "kv_cache", "weights", "context_lens", "block_table"):
+        if k in data:
+            dev[k] = torch.from_numpy(np.ascontiguousarray(data[k])).cuda()
+    return dev
+
+
+def run(data, dev=None, num_workers=None, out=None, schedule=None):
+    """Schedule + logits on the GPU; returns (logits float32 numpy, schedule)."""
+    dev = upload(data) if dev is None else dev
+    variant = pmqa.VARIANT_FP8 if data["variant"] == "fp8" else pmqa.VARIANT_FP4
+    nn = int(data["next_n"])
+    if schedule is None:
+        schedule = pmqa.compute_schedule(dev["context_lens"], num_workers=num_workers,
+                                         variant=variant, next_n=nn)
+    M = int(data["max_context_len"])
+    if variant == pmqa.VARIANT_FP8:
+        lg = pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                       dev["context_lens"], dev["block_table"], schedule, M,
+                                       out=out)
+    else:
+        lg = pmqa.paged_mqa_logits_fp4(dev["q"], dev["q_scale"], dev["kv_cache"],
+                                       dev["weights"], dev["context_lens"], dev["block_table"],
+                                       schedule, M, out=out)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), schedule
+
+
+def oracle(data, rows=None):
+    from oracle import reference
+    if data["variant"] == "fp8":
+        return reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"],
+                                              data["context_lens"], data["block_table"],
+                                              data["max_context_len"], rows=rows, want_tol=True)
+    return reference.paged_mqa_logits_fp4(data["q"], data["q_scale"], data["kv_cache"],
+                                          data["weights"], data["context_lens"],
+                                          data["block_table"], data["max_context_len"],
+                                          rows=rows, want_tol=True)
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)

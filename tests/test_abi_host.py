@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol and rejects bad arguments before touching a device (runs without GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pmqa.h")
+
+pmqa = pytest.importorskip("paged_mqa_logits_amd",
+                           reason="libpmqa.so not built (python -m paged_mqa_logits_amd.build)")
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert set(names) == set(pmqa.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pmqa.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_schedule_bytes():
+    assert pmqa.schedule_bytes(4, 3) == 4 * (8 + 2 * 4 + 4 + 1)
+    assert pmqa.schedule_bytes(2048, 3072) == 4 * (8 + 2 * 3073 + 2049)
+    assert pmqa.schedule_bytes(0, 3) == 0
+    assert pmqa.schedule_bytes(3, 0) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails first
+
+
+def _fp8(lib, **kw):
+    args = dict(q=FAKE, kv=FAKE, w=FAKE, ctx=FAKE, bt=FAKE, sched=FAKE, out=FAKE, batch=2,
+                next_n=1, heads=64, dim=128, page=64, num_pages=10, bt_stride=4, max_ctx=256,
+                ldo=256, workers=8)
+    args.update(kw)
+    p = ctypes.c_void_p
+    return lib.paged_mqa_logits_fp8(
+        p(args["q"]), p(args["kv"]), p(args["w"]), p(args["ctx"]), p(args["bt"]),
+        p(args["sched"]), p(args["out"]), args["batch"], args["next_n"], args["heads"],
+        args["dim"], args["page"], args["num_pages"], args["bt_stride"], args["max_ctx"],
+        args["ldo"], args["workers"], p(0))
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), 1, "q is null"),
+    (dict(kv=0), 1, "kv_cache is null"),
+    (dict(w=0), 1, "weights is null"),
+    (dict(ctx=0), 1, "context_lens is null"),
+    (dict(bt=0), 1, "block_table is null"),
+    (dict(sched=0), 1, "schedule is null"),
+    (dict(out=0), 1, "logits is null"),
+    (dict(q=FAKE + 4), 1, "q must be 16-byte aligned"),
+    (dict(out=FAKE + 8), 1, "logits must be 16-byte aligned"),
+    (dict(ctx=FAKE + 2), 1, "4-byte aligned"),
+    (dict(batch=0), 1, "batch"),
+    (dict(heads=32), 2, "not compiled"),
+    (dict(dim=64), 2, "not compiled"),
+    (dict(page=16), 2, "not compiled"),
+    (dict(next_n=3), 2, "next_n = 3"),
+    (dict(num_pages=0), 1, "num_pages"),
+    (dict(bt_stride=0), 1, "block_table_stride"),
+    (dict(max_ctx=0), 1, "max_context_len"),
+    (dict(ldo=100), 1, "logits_stride"),
+    (dict(ldo=258), 1, "multiple of 4"),
+    (dict(workers=0), 1, "num_workers"),
+])
+def test_fp8_argument_checks(kw, status, needle):
+    lib = pmqa.library()
+    st = _fp8(lib, **kw)
+    assert st == status, (st, pmqa.last_error())
+    assert needle in pmqa.last_error()
+
+
+def test_fp4_null_q_scale():
+    lib = pmqa.library()
+    p = ctypes.c_void_p
+    st = lib.paged_mqa_logits_fp4(p(FAKE), p(0), p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                  p(FAKE), 2, 1, 64, 128, 64, 10, 4, 256, 256, 8, p(0))
+    assert st == 1 and "q_scale is null" in pmqa.last_error()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((0, 4, 8, FAKE), "context_lens is null"),
+    ((FAKE, 4, 8, 0), "schedule is null"),
+    ((FAKE, 0, 8, FAKE), "batch"),
+    ((FAKE, 4, 0, FAKE), "num_workers"),
+    ((FAKE + 1, 4, 8, FAKE), "aligned"),
+])
+def test_schedule_argument_checks(args, needle):
+    lib = pmqa.library()
+    p = ctypes.c_void_p
+    ctx, B, W, out = args
+    st = lib.compute_schedule(p(ctx), B, W, p(out), p(0))
+    assert st == 1 and needle in pmqa.last_error()
+
+
+def test_default_num_workers_argument_checks():
+    lib = pmqa.library()
+    out = ctypes.c_int32(0)
+    assert lib.pmqa_default_num_workers(0, 5, 1, ctypes.byref(out)) == 1
+    assert lib.pmqa_default_num_workers(0, 0, 3, ctypes.byref(out)) == 2
+    assert lib.pmqa_default_num_workers(0, 0, 1, None) == 1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pmqa.paged_mqa_logits_fp8(q, q, q, q, q, q, 16)

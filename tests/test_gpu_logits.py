@@ -1,0 +1,199 @@
+"""GPU parity of paged_mqa_logits_fp8 / _fp4 against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import golden_fixtures as gf
+import parity
+from gpu_util import announce, oracle, run, upload
+from workloads import CONFIGS, make_fp4, make_fp8, make_workload
+
+pytestmark = pytest.mark.gpu
+pmqa = pytest.importorskip("paged_mqa_logits_amd")
+
+
+# ---------------------------------------------------------------- fixtures
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_hand_fixture_fp8(case):
+    announce(f"hand fixture fp8 case {case}")
+    e = gf.embed_fp8(gf.load_fp8(case))
+    e["variant"] = "fp8"
+    lg, _ = run(e)
+    assert np.array_equal(lg.astype(np.float64), e["expected"]), lg
+
+
+def test_hand_fixture_fp4():
+    announce("hand fixture fp4")
+    e = gf.embed_fp4(gf.load_fp4())
+    e["variant"] = "fp4"
+    lg, _ = run(e)
+    assert np.array_equal(lg.astype(np.float64), e["expected"]), lg
+
+
+# ---------------------------------------------------------------- full compare
+
+EDGE_CTX = [0, 1, 2, 63, 64, 65, 127, 255, 256, 257, 300, 511, 512, 513, 700, 1000, 1023, 1024]
+
+
+@pytest.mark.parametrize("next_n", [1, 2])
+@pytest.mark.parametrize("negative_scales", [False, True])
+def test_fp8_edge_lengths(next_n, negative_scales):
+    announce(f"fp8 edge lengths nn={next_n} neg={negative_scales}")
+    d = make_fp8(EDGE_CTX, next_n=next_n, max_context_len=1024, seed=21 + next_n,
+                 negative_scales=negative_scales)
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "fp8 edge")
+
+
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_fp4_edge_lengths(next_n):
+    announce(f"fp4 edge lengths nn={next_n}")
+    d = make_fp4(EDGE_CTX, next_n=next_n, max_context_len=1024, seed=31 + next_n)
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "fp4 edge")
+
+
+def test_tiny_config():
+    announce("tiny_fp8 config")
+    d = make_workload("tiny_fp8")
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "tiny_fp8")
+
+
+@pytest.mark.parametrize("M", [1, 5, 100, 255, 257, 1000])
+def test_fp8_truncation_and_odd_widths(M):
+    announce(f"fp8 truncation M={M}")
+    d = make_fp8([0, 3, 200, 900, 1100], next_n=1, max_context_len=M, seed=40 + M,
+                 bt_stride=-(-1100 // 64))
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), f"trunc M={M}")
+
+
+def test_zero_rows_interleaved_at_worker_boundaries():
+    """Zero-length rows between every non-empty row and many workers, so that
+    worker ranges start right after skipped rows."""
+    announce("zero rows interleaved")
+    ctx = []
+    for i in range(40):
+        ctx += [0, 0, 256 * (i % 3) + 17 * i + 1]
+    d = make_fp8(ctx, max_context_len=1024, seed=50)
+    ref = oracle(d)
+    for W in (1, 5, 37, 128, 1000):
+        lg, _ = run(d, num_workers=W)
+        parity.check(lg, ref, f"zero rows W={W}")
+
+
+def test_all_rows_empty():
+    announce("all rows empty")
+    d = make_fp8([0, 0, 0, 0], max_context_len=300, seed=51)
+    lg, _ = run(d)
+    assert np.all(lg.view(np.uint32) == parity.NEG_INF_BITS)
+
+
+def test_mid_config_full():
+    announce("mid_fp8 config (full compare)")
+    d = make_workload("mid_fp8")
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "mid_fp8")
+
+
+def test_fp4_small_full():
+    announce("fp4 small full compare")
+    rng = np.random.default_rng(60)
+    ctx = rng.integers(0, 5000, size=24)
+    ctx[::5] = 0
+    d = make_fp4(ctx, max_context_len=5000, seed=60)
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "fp4 small")
+
+
+# ---------------------------------------------------------------- self-consistency
+
+def test_worker_count_invariance_and_determinism():
+    announce("worker-count invariance")
+    rng = np.random.default_rng(70)
+    ctx = rng.integers(0, 3000, size=50)
+    ctx[rng.random(50) < 0.3] = 0
+    d = make_fp8(ctx, next_n=2, max_context_len=3000, seed=70)
+    dev = upload(d)
+    base, _ = run(d, dev=dev)
+    again, _ = run(d, dev=dev)
+    assert np.array_equal(base.view(np.uint32), again.view(np.uint32))
+    for W in (1, 37, 256, 1024, 8192):
+        lg, _ = run(d, dev=dev, num_workers=W)
+        assert np.array_equal(base.view(np.uint32), lg.view(np.uint32)), W
+
+
+def test_weight_doubling_is_exact():
+    announce("weights x2")
+    d = make_fp8([500, 70, 0, 1000], max_context_len=1000, seed=71)
+    base, _ = run(d)
+    d2 = dict(d, weights=(2 * d["weights"]).astype(np.float32))
+    twice, _ = run(d2)
+    assert np.array_equal(twice, 2 * base)
+
+
+def test_page_permutation_invariance():
+    announce("page permutation")
+    d = make_fp8([900, 333, 64, 0, 1024], next_n=2, max_context_len=1024, seed=72)
+    rng = np.random.default_rng(72)
+    perm = rng.permutation(d["kv_cache"].shape[0])
+    kv = np.empty_like(d["kv_cache"])
+    kv[perm] = d["kv_cache"]
+    d2 = dict(d, kv_cache=kv, block_table=perm[d["block_table"]].astype(np.int32))
+    a, _ = run(d)
+    b, _ = run(d2)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_columns_past_max_context_untouched():
+    announce("guard columns")
+    d = make_fp8([100, 0, 300], next_n=2, max_context_len=301, seed=73)
+    dev = upload(d)
+    out = torch.full((6, 320), 12345.0, dtype=torch.float32, device="cuda")
+    sched = pmqa.compute_schedule(dev["context_lens"])
+    pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], dev["context_lens"],
+                              dev["block_table"], sched, 301, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, 301:] == 12345.0)
+    parity.check(o[:, :301], oracle(d), "guard")
+
+
+# ---------------------------------------------------------------- full sizes (sampled rows)
+
+def _sample_rows(d, k, seed):
+    ctx = d["context_lens"]
+    nn = d["next_n"]
+    B = len(ctx)
+    rng = np.random.default_rng(seed)
+    picks = set(rng.choice(B, size=min(k, B), replace=False).tolist())
+    picks |= {int(np.argmax(ctx)), int(np.argmin(ctx)), 0, B - 1}
+    zero = np.nonzero(ctx == 0)[0]
+    if len(zero):
+        picks.add(int(zero[0]))
+    return sorted(r for b in picks for r in range(b * nn, b * nn + nn))
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", ["large_fp8", "spec_fp8", "mxfp4"])
+def test_full_size_config_sampled(name):
+    """Full configuration in the launch configuration the benchmark times
+    (default worker count); sampled rows against the oracle, and every row's
+    mask checked against its context length."""
+    announce(f"{name} full size (sampled rows)")
+    d = make_workload(name)
+    lg, _ = run(d)
+    rows = _sample_rows(d, 12, seed=CONFIGS[name].seed)
+    parity.check(lg[rows], oracle(d, rows=rows), name)
+    # mask of every row, from the context lengths alone
+    M = d["max_context_len"]
+    nn = d["next_n"]
+    ctx = d["context_lens"].astype(np.int64)
+    lim = np.clip(np.repeat(ctx, nn) - nn + 1 + np.tile(np.arange(nn), len(ctx)), 0, M)
+    cols = np.arange(M)[None, :]
+    masked = cols >= lim[:, None]
+    bits = lg.view(np.uint32)
+    assert np.all(bits[masked] == parity.NEG_INF_BITS)
+    assert np.all(np.isfinite(lg[~masked]))

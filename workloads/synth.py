@@ -9,11 +9,15 @@ drawn in this fixed order):
 3. physical pages: ``perm = rng.permutation(pool)``; logical pages of all rows
    in row-major order take ``perm[0], perm[1], ...``; the remaining pool pages
    are poison pages;
-4. q ~ N(0, 1) (float32), quantized to the variant's element format;
-5. K rows ~ N(0, 1) (float32), drawn row by row in token order and quantized
-   per token (fp8: scale = amax/448, values = e4m3(k/scale)) or per 32-element
-   block (MXFP4, shared exponent floor(log2 amax) - 2);
-6. head weights ~ N(0, 1) / sqrt(H) (float32).
+4. a 63-bit seed for a ``torch.Generator`` that draws the bulk normals
+   (torch's CPU sampler is several times faster than numpy's and gives the
+   same stream for any thread count or chunking);
+5. q ~ N(0, 1) (float32, torch stream), quantized to the variant's format;
+6. K rows ~ N(0, 1) (float32, torch stream), drawn row by row in token order
+   and quantized per token (fp8: scale = amax/448, values = e4m3(k/scale)) or
+   per 32-element block (MXFP4, shared exponent floor(log2 amax) - 2);
+7. with ``negative_scales`` (fp8 tests only), the signs of the token scales;
+8. head weights ~ N(0, 1) / sqrt(H) (float32, numpy stream).
 
 Bytes that no correct implementation reads hold large finite poison: unused
 pool pages, the slots of a row's last page at or beyond its context length,
@@ -21,8 +25,8 @@ and block-table entries past a row's last page (they name poison pages).  A
 stray read therefore produces a huge wrong value, never a fault.
 
 Quantization uses torch's float8_e4m3fn cast (round to nearest even; inputs
-are clamped to +-448 first) and, for E2M1, a round-to-nearest-even search over
-the eight magnitudes with saturation at 6.  Quantization only shapes the input
+are clamped to +-448 first) and, for E2M1, round-half-to-even on the E2M1 grid
+with saturation at 6.  Quantization only shapes the input
 data: the oracle and the GPU read the same bytes.
 """
 from dataclasses import dataclass, replace
@@ -106,15 +110,24 @@ def quantize_e4m3(x: np.ndarray) -> np.ndarray:
 
 def quantize_fp8_tokens(k: np.ndarray):
     """Per-token fp8 quantization: (bytes uint8 [n, D], scale float32 [n])."""
-    amax = np.max(np.abs(k), axis=1).astype(np.float32)
-    scale = (amax / np.float32(448.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    codes = quantize_e4m3(k / safe[:, None])
+    t = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float32))
+    amax = t.abs().amax(dim=1)
+    scale = amax / 448.0
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    codes = (t / safe[:, None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     codes[scale == 0] = 0
-    return codes, scale
+    return codes.numpy(), scale.numpy().astype(np.float32)
 
 
-_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+# Rounding boundaries between consecutive E2M1 magnitudes (0, 0.5, 1, 1.5, 2,
+# 3, 4, 6).  A value equal to a midpoint rounds to the even code: the
+# midpoints above an odd code are moved down by one ulp so that, with
+# bucketize's "boundary[i-1] < v <= boundary[i]" rule, ties go up there and
+# down everywhere else.  The bucket index is the E2M1 magnitude code.
+_E2M1_BOUNDS = torch.tensor([0.25, np.nextafter(np.float32(0.75), np.float32(0)), 1.25,
+                             np.nextafter(np.float32(1.75), np.float32(0)), 2.5,
+                             np.nextafter(np.float32(3.5), np.float32(0)), 5.0],
+                            dtype=torch.float32)
 
 
 def quantize_mxfp4(x: np.ndarray):
@@ -122,26 +135,33 @@ def quantize_mxfp4(x: np.ndarray):
 
     Shared exponent per 32 consecutive elements: floor(log2 amax) - 2 (the
     largest E2M1 exponent is 2), clamped to [-127, 127]; an all-zero block
-    gets code 0.  Elements are rounded to nearest even and saturate at 6.
+    gets code 0.  Each scaled element (an exact power-of-two rescale) is
+    rounded to the nearest E2M1 magnitude, ties to the even code, and
+    saturates at 6.
     """
     x = np.asarray(x, dtype=np.float32)
     shp = x.shape
     D = shp[-1]
-    blk = x.reshape(-1, D // 32, 32)
-    amax = np.max(np.abs(blk), axis=2)
-    _, e = np.frexp(amax)                      # amax = m * 2^e, m in [0.5, 1)
-    ex = np.clip(e.astype(np.int32) - 1 - 2, -127, 127)
-    code_s = np.where(amax > 0, ex + 127, 0).astype(np.uint8)
-    inv = np.ldexp(np.float32(1.0), -ex).astype(np.float32)
-    v = blk * inv[..., None]
-    a = np.abs(v)
-    code = np.searchsorted(_E2M1_MID, a, side="left").astype(np.uint8)
-    at_mid = (code < 7) & (a == _E2M1_MID[np.minimum(code, 6)])
-    code = np.where(at_mid & (code % 2 == 1), code + 1, code).astype(np.uint8)
-    code = np.where((v < 0) & (code > 0), code | 8, code).astype(np.uint8)
+    blk = torch.from_numpy(np.ascontiguousarray(x)).reshape(-1, D // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    ex = (torch.frexp(amax).exponent - 3).clamp_(-127, 127)     # floor(log2 amax) - 2
+    code_s = torch.where(amax > 0, ex + 127, torch.zeros_like(ex)).to(torch.uint8)
+    v = blk * torch.ldexp(torch.ones_like(amax), -ex)[..., None]
+    code = torch.bucketize(v.abs(), _E2M1_BOUNDS, out_int32=True).to(torch.uint8)
+    code |= ((v < 0) & (code > 0)).to(torch.uint8) << 3
     code = code.reshape(-1, D)
-    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return packed.reshape(shp[:-1] + (D // 2,)), code_s.reshape(shp[:-1] + (D // 32,))
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return (packed.numpy().reshape(shp[:-1] + (D // 2,)),
+            code_s.numpy().reshape(shp[:-1] + (D // 32,)))
+
+
+def _torch_normals(rng):
+    g = torch.Generator()
+    g.manual_seed(int(rng.integers(0, 2 ** 63 - 1)))
+
+    def draw(*shape):
+        return torch.randn(shape, generator=g, dtype=torch.float32).numpy()
+    return draw
 
 
 def _pages_needed(ctx, page_size):
@@ -184,7 +204,8 @@ def make_fp8(context_lens, next_n=1, max_context_len=None, seed=0, pool_factor=1
         bt_stride = max(1, -(-max(M, int(ctx.max(initial=0))) // page_size))
     H, D, P = num_heads, head_dim, page_size
     bt, pool, npg = _layout_pages(rng, ctx, P, pool_factor, bt_stride)
-    q = quantize_e4m3(rng.standard_normal((B, next_n, H, D), dtype=np.float32))
+    normal = _torch_normals(rng)
+    q = quantize_e4m3(normal(B, next_n, H, D))
     vbytes = P * D
     kv = np.empty((pool, vbytes + 4 * P), dtype=np.uint8)
     kv[:, :vbytes] = FP8_POISON_VALUE
@@ -194,7 +215,7 @@ def make_fp8(context_lens, next_n=1, max_context_len=None, seed=0, pool_factor=1
         if L == 0:
             continue
         n = int(npg[b])
-        codes, scale = quantize_fp8_tokens(rng.standard_normal((L, D), dtype=np.float32))
+        codes, scale = quantize_fp8_tokens(normal(L, D))
         vals = np.full((n * P, D), FP8_POISON_VALUE, dtype=np.uint8)
         vals[:L] = codes
         sc = np.full(n * P, FP8_POISON_SCALE, dtype="<f4")
@@ -226,7 +247,8 @@ def make_fp4(context_lens, next_n=1, max_context_len=None, seed=0, pool_factor=1
         bt_stride = max(1, -(-max(M, int(ctx.max(initial=0))) // page_size))
     H, D, P = num_heads, head_dim, page_size
     bt, pool, npg = _layout_pages(rng, ctx, P, pool_factor, bt_stride)
-    q, q_scale = quantize_mxfp4(rng.standard_normal((B, next_n, H, D), dtype=np.float32))
+    normal = _torch_normals(rng)
+    q, q_scale = quantize_mxfp4(normal(B, next_n, H, D))
     vbytes = P * D // 2
     sbytes = P * D // 32
     kv = np.empty((pool, vbytes + sbytes), dtype=np.uint8)
@@ -237,7 +259,7 @@ def make_fp4(context_lens, next_n=1, max_context_len=None, seed=0, pool_factor=1
         if L == 0:
             continue
         n = int(npg[b])
-        packed, scl = quantize_mxfp4(rng.standard_normal((L, D), dtype=np.float32))
+        packed, scl = quantize_mxfp4(normal(L, D))
         vals = np.full((n * P, D // 2), FP4_POISON_VALUE, dtype=np.uint8)
         vals[:L] = packed
         ss = np.full((n * P, D // 32), FP4_POISON_SCALE, dtype=np.uint8)
