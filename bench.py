@@ -1,0 +1,257 @@
+"""Benchmark: fp8 paged MQA logits at batch-2048 decode on one MI355X.
+
+One step is the whole hot path for one decode batch: compute_schedule
+followed by paged_mqa_logits_fp8, replayed from a captured HIP graph, with all
+inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (seeded, synthetic; see workloads/synth.py): B = 2048 rows, next_n 1,
+64 heads, head_dim 128, 64-token pages; context lengths lognormal (median
+4096, sigma 1) clipped to [1, 65536] with 10% of rows empty; output width
+65536.
+
+Reported beside the step rate:
+  roofline      the logits kernel alone, timed with HIP events on the stream
+                it is launched on: algorithmic bytes per launch / mean launch
+                duration, against the 8 TB/s HBM peak; ``traffic`` is read from
+                the rocprofv3 counter summary in profiles/ when that summary was
+                taken on the current kernel sources, else null;
+  cpu_baseline  the fp64 CPU oracle on a fixed subset of the same rows.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV tokens scored/s + achieved HBM GB/s, fp8 paged MQA logits, B=2048 decode"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "large_fp8"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_fp8_large_fp8_traffic.txt")
+KERNEL_SOURCES = ["logits_kernel.hpp", "logits_fp8.hip", "pmqa_internal.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_mqa_logits_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(ctx, next_n, max_ctx, heads, dim, page, sched_bytes):
+    """Bytes the method must move for one logits call (partial pages not counted)."""
+    ctx = ctx.astype(np.int64)
+    B = len(ctx)
+    k_stream = (dim + 4) * int(ctx.sum())                  # e4m3 row + fp32 scale per token
+    table = 4 * int(((ctx + page - 1) // page).sum())      # block-table entries read
+    qw = B * next_n * heads * (dim + 4)                     # q bytes + fp32 weights
+    out = 4 * B * next_n * max_ctx                          # every logit, -inf included
+    return k_stream + table + qw + 4 * B + out + sched_bytes
+
+
+def scored_tokens(ctx, next_n, max_ctx):
+    lim = np.repeat(ctx.astype(np.int64), next_n) - next_n + 1 + np.tile(np.arange(next_n), len(ctx))
+    return int(np.clip(lim, 0, max_ctx).sum())
+
+
+def read_traffic(expected_hash, launches_bytes):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != expected_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(data, n_rows, seed):
+    """Time the fp64 oracle on a fixed random subset of rows."""
+    from oracle import reference
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = len(os.sched_getaffinity(0))
+    B = len(data["context_lens"])
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(B, size=min(n_rows, B), replace=False))
+    t0 = time.perf_counter()
+    reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"],
+                                   data["context_lens"], data["block_table"],
+                                   data["max_context_len"], rows=rows.tolist())
+    dt = time.perf_counter() - t0
+    toks = int(data["context_lens"][rows].astype(np.int64).sum())
+    return {"value": toks / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{len(rows)} of {B} rows (seeded), {toks} KV tokens, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the workload timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this size "
+                         "(reference kernel for rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_mqa_logits_amd as pmqa
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[WORKLOAD]
+    print(f"[bench] generating {WORKLOAD}", file=sys.stderr, flush=True)
+    data = make_workload(WORKLOAD)
+    ctx_np = data["context_lens"]
+    M = data["max_context_len"]
+    NN = data["next_n"]
+    B = len(ctx_np)
+    torch.cuda.set_device(0)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(data[k])).cuda()
+           for k in ("q", "kv_cache", "weights", "context_lens", "block_table")}
+    W = pmqa.default_num_workers(pmqa.VARIANT_FP8, NN)
+    sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty((B * NN, M), dtype=torch.float32, device="cuda")
+
+    def step():
+        pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
+        pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], dev["context_lens"],
+                                  dev["block_table"], sched, M, out=out, num_workers=W)
+
+    step()
+    torch.cuda.synchronize()
+    print("[bench] eager step ok; capturing graph", file=sys.stderr, flush=True)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] graph step {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # logits kernel alone, events on the stream it is launched on
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], dev["context_lens"],
+                                  dev["block_table"], sched, M, out=out, num_workers=W)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)])
+    k_mean = float(k_ms.mean())
+    # schedule kernel alone
+    es0 = torch.cuda.Event(enable_timing=True)
+    es1 = torch.cuda.Event(enable_timing=True)
+    es0.record(stream)
+    for _ in range(args.steps):
+        pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
+    es1.record(stream)
+    torch.cuda.synchronize()
+    s_mean = es0.elapsed_time(es1) / args.steps
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # sampled parity of the last output against the oracle
+    from oracle import reference
+    rows = [int(np.argmax(ctx_np)), int(np.nonzero(ctx_np == 0)[0][0]) if (ctx_np == 0).any() else 0, 1, B - 1]
+    ref = reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"], ctx_np,
+                                         data["block_table"], M, rows=rows, want_tol=True)
+    got = out[rows].cpu().numpy()
+    masked = np.isneginf(ref["logits"])
+    ok = bool(np.all(got.view(np.uint32)[masked] == np.uint32(0xFF800000)) and
+              np.all(np.abs(got[~masked].astype(np.float64) - ref["logits"][~masked]) <= ref["tol"][~masked]))
+
+    tokens = scored_tokens(ctx_np, NN, M)
+    sbytes = pmqa.schedule_bytes(B, W)
+    alg = algorithmic_bytes(ctx_np, NN, M, pmqa.NUM_HEADS, pmqa.HEAD_DIM, pmqa.PAGE_SIZE, sbytes)
+    achieved = alg / (k_mean * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash, alg)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(data, args.cpu_rows, seed=cfg.seed)
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": ("large_fp8: B=2048 decode, next_n=1, 64 heads, head_dim 128, 64-token "
+                         "pages, ctx lognormal(median 4096, sigma 1) clipped [1, 65536], 10% "
+                         "empty rows, logits [2048, 65536] fp32; step = graph replay of "
+                         "compute_schedule + paged_mqa_logits_fp8"),
+            "batch": B, "next_n": NN, "max_context_len": M, "kv_tokens_per_step": tokens,
+            "num_workers": W, "graph": True,
+        },
+        "gbps": alg / (ms_step * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": alg,
+        "logits_kernel_us": {"mean": k_mean * 1e3, "p10": float(np.percentile(k_ms, 10)) * 1e3,
+                             "p90": float(np.percentile(k_ms, 90)) * 1e3},
+        "schedule_kernel_us": s_mean * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "logits_kernel<Fp8Format, 1>", "kernel_source_hash": src_hash},
+        "sampled_parity": ok,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
