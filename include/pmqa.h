@@ -130,7 +130,7 @@ pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32
  *   context_lens  int32 [batch].
  *   block_table   int32 [batch, block_table_stride]; entry i of row b names
  *                 the physical page of tokens [64i, 64i+64).  Only entries
- *                 i < ceil(ctx_b/64) are read.
+ *                 i < ceil(ctx_b/64) are used (others of the row may be read).
  *   schedule      from compute_schedule(context_lens, batch, num_workers).
  *   logits        fp32 [batch*next_n, logits_stride], 16-B aligned,
  *                 logits_stride % 4 == 0 and >= max_context_len.  Row

@@ -16,7 +16,7 @@
 #include <atomic>
 #include <vector>
 
-#include "../../include/pmqa.h"
+#include "pmqa.h"
 #include "pmqa_internal.h"
 
 namespace {
@@ -39,6 +39,8 @@ pmqa_status_t ok() {
 constexpr int kMaxDevices = 64;
 // 0 = not checked, 1 = gfx950, 2 = other architecture
 std::atomic<int> g_arch[kMaxDevices];
+// compute units per device (0 = not queried yet)
+std::atomic<int> g_cus[kMaxDevices];
 
 pmqa_status_t check_device(int* dev_out) {
   int dev = 0;
@@ -53,6 +55,8 @@ pmqa_status_t check_device(int* dev_out) {
     if (e != hipSuccess)
       return fail(PMQA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                     std::memory_order_release);
     g_arch[dev].store(st, std::memory_order_release);
   }
   if (st != 1) return fail(PMQA_ERR_UNSUPPORTED, "device %d is not a gfx950 (MI355X)", dev);
@@ -88,8 +92,8 @@ pmqa_status_t check_shape(const Shape& s, int32_t num_heads, int32_t head_dim, i
     return fail(PMQA_ERR_INVALID_ARGUMENT, "num_pages = %lld must be >= 1", (long long)s.num_pages);
   if (s.bt_stride < 1)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "block_table_stride = %d must be >= 1", s.bt_stride);
-  if (s.max_ctx < 1)
-    return fail(PMQA_ERR_INVALID_ARGUMENT, "max_context_len = %d must be >= 1", s.max_ctx);
+  if (s.max_ctx < 1 || s.max_ctx > (1 << 29))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "max_context_len = %d must be in [1, 2^29]", s.max_ctx);
   if (s.ldo < s.max_ctx)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "logits_stride = %lld < max_context_len = %d",
                 (long long)s.ldo, s.max_ctx);
@@ -180,7 +184,8 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
                 "context_lens, block_table and schedule must be 4-byte aligned");
   pmqa_status_t st = check_shape(s, num_heads, head_dim, page_size);
   if (st != PMQA_OK) return st;
-  st = check_device(nullptr);
+  int dev = 0;
+  st = check_device(&dev);
   if (st != PMQA_OK) return st;
   if (validate_mode()) {
     st = validate_contents(ctx, bt, sched, s, stream);
@@ -201,9 +206,12 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
   a.bt_stride = s.bt_stride;
   a.max_ctx = s.max_ctx;
   a.num_workers = s.workers;
-  const hipError_t e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
-                                                   : pmqa::launch_logits_fp4(a, s.next_n, stream);
+  hipError_t e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
+                                             : pmqa::launch_logits_fp4(a, s.next_n, stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
+  e = pmqa::launch_tail_fill(logits, s.ldo, s.batch, s.next_n, s.max_ctx, sched, s.workers,
+                             g_cus[dev].load(std::memory_order_acquire), stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "tail fill launch: %s", hipGetErrorString(e));
   return ok();
 }
 

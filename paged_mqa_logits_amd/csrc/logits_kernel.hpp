@@ -9,16 +9,16 @@
 // Mapping onto CDNA4
 // ------------------
 // One worker is one 64-lane wavefront.  A worker walks its schedule range of
-// 256-token units page by page (64 tokens).  For a page it contracts the
-// 64-head query block of each query row against the page's 64 K rows with
+// 256-token units; a unit is 4 pages of 64 tokens.  For a page it contracts
+// the 64-head query block of each query row against the page's 64 K rows with
 // v_mfma_scale_f32_16x16x128_f8f6f4: K = head_dim = 128 is covered by one
 // instruction, so a page is 4 head groups x 4 token groups x next_n MFMAs.
 //
 //   A operand (query): lane l holds head 16*hg + (l & 15), elements
 //     [32*(l>>4), +32) of head_dim.  Loaded once per batch row.
 //   B operand (K):     lane l holds token 16*tg + (l & 15), the same element
-//     range.  Loaded straight from HBM into VGPRs with 16-byte loads: every
-//     K byte is used by exactly one lane, so no LDS staging is needed.
+//     range.  Loaded straight from HBM into VGPRs with 16-byte buffer loads:
+//     every K byte is used by exactly one lane, so no LDS staging is needed.
 //   C (scores):        lane l holds heads 16*hg + 4*(l>>4) + i, i = 0..3, of
 //     token 16*tg + (l & 15).
 //
@@ -28,14 +28,24 @@
 // with permlane32/permlane16 swaps so that lane l ends up owning token l of
 // the page and the 64 results are stored as one contiguous 256-byte row.
 //
-// Software pipeline: the K fragment of the next page is requested before the
-// current page is contracted.  Both the lookahead and the consumer use the
-// same iterator function, so they always agree on which (row, unit, page)
-// comes next, including across skipped zero-length rows.
+// Memory pipeline
+// ---------------
+// One worker wavefront runs per SIMD (the kernel is sized for 4 wavefronts
+// per compute unit), which leaves registers for a ring of 4 K pages: while
+// a unit's 4 pages are consumed, the next unit's 4 pages are in flight.
+// K pages are read through buffer resources.  A page with no data to score
+// (past the context, or past the block table) gets a zero-size resource, so
+// its loads return zeros without touching memory, and output rows are stored
+// through a resource sized to max_context_len, so columns past it are dropped
+// by the hardware.  Every page therefore issues the same memory instructions,
+// which lets the compiler wait for exactly the page being consumed while the
+// next one is in flight (double buffering in VGPRs).  The block-table entries
+// of the next unit are requested at the start of the current one.  The
+// lookahead and the consumer walk the same iterator, so they always agree on
+// which (row, unit) comes next, including across skipped zero-length rows.
 //
-// After its units, every worker writes -inf over an equal share of the
-// 256-column chunks that lie past each row's last unit (the tail fill), with
-// 16-byte non-temporal stores.
+// Columns past each row's last unit are written with -inf by a separate
+// kernel (tail_fill.hip) launched right after this one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,21 +58,33 @@ namespace pmqa {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kFmtFp8 = 0;  // cbsz/blgp code of E4M3 operands
-constexpr int kFmtFp4 = 4;  // cbsz/blgp code of E2M1 operands
+constexpr int kFmtFp8 = 0;      // cbsz/blgp code of E4M3 operands
+constexpr int kFmtFp4 = 4;      // cbsz/blgp code of E2M1 operands
 constexpr int kScaleOne = 127;  // E8M0 encoding of 1.0
+// Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Wave-uniform read of read-only metadata (schedule, context lengths, block
+// table) through the constant address space, so it is a scalar load that
+// waits on lgkmcnt only and never on the vector loads in flight.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 
 __device__ __forceinline__ int32_t sload(const int32_t* p) {
-  return __builtin_amdgcn_readfirstlane(*p);
+  return __builtin_amdgcn_readfirstlane(*(cint_ptr)(p));
+}
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
 }
 
 // Read-only view of a schedule; every index derived from it is clamped.
 struct SchedView {
   const int32_t* starts;
   const int32_t* S;
-  int32_t rows;      // batch rows covered (0 when the schedule is unusable)
-  int32_t cap;       // units per row never exceed ceil(max_ctx / 256)
+  int32_t rows;  // batch rows covered (0 when the schedule is unusable)
+  int32_t cap;   // units per row never exceed ceil(max_ctx / 256)
 };
 
 __device__ __forceinline__ SchedView make_view(const LogitsArgs& a) {
@@ -84,78 +106,71 @@ __device__ __forceinline__ int32_t units_of(const SchedView& v, int32_t b) {
   return min(max(c, 0), v.cap);
 }
 
-// One page of work: batch row b, unit u, page p of the unit (0..3).  b ==
-// rows marks the end.  len is the row's current context length.
-struct Task {
-  int32_t b, u, p, len;
+// One unit of work: batch row b, unit u (tokens [256u, 256u + 256)).
+// b == rows marks the end.  len is the row's current context length, units
+// its unit count, raw the block-table entries of the unit's 4 pages as read
+// (validated and clamped only where they are used, so the scalar loads that
+// fetch them one unit ahead are not waited for early).
+struct Unit {
+  int32_t b, u, len, units;
+  int32_t raw[kPagesPerUnit];
 };
 
-// Task iterator: the single definition of "what comes next" used by both the
-// K lookahead and the consumer.
+// Task iterator: the single definition of "what comes next", used both for
+// the lookahead (block-table entries and first page of the next unit) and
+// for the unit being consumed.
 struct Iter {
   SchedView v;
-  const int32_t* ctx;
+  const LogitsArgs* a;
   int32_t end_b, end_u;
-  int32_t max_ctx;
 
-  __device__ __forceinline__ bool in_range(int32_t b, int32_t u) const {
-    return b < v.rows && (b < end_b || (b == end_b && u < end_u));
-  }
-  __device__ __forceinline__ Task make(int32_t b, int32_t u) const {
-    Task t;
-    if (in_range(b, u)) {
-      t.b = b;
-      t.u = u;
-      t.p = 0;
-      t.len = sload(ctx + b);
-    } else {
-      t.b = v.rows;
-      t.u = t.p = t.len = 0;
-    }
+  __device__ __forceinline__ bool valid(const Unit& t) const { return t.b < v.rows; }
+
+  __device__ __forceinline__ Unit make(int32_t b, int32_t u, int32_t len, int32_t units) const {
+    Unit t;
+    const bool in = b < v.rows && (b < end_b || (b == end_b && u < end_u));
+    t.b = in ? b : v.rows;
+    t.u = u;
+    t.len = len;
+    t.units = units;
+    // Unconditional loads of in-bounds entries: the row index is clamped to
+    // the table and the column to the row, whatever the unit holds.
+    const int32_t bb = min(b, a->batch - 1);
+    const int64_t row = (int64_t)bb * a->bt_stride;
+#pragma unroll
+    for (int p = 0; p < kPagesPerUnit; ++p)
+      t.raw[p] = sload(a->bt + row + min(u * kPagesPerUnit + p, a->bt_stride - 1));
     return t;
   }
-  // Next unit after (b, u), skipping rows that have no unit.
-  __device__ __forceinline__ Task next_unit(int32_t b, int32_t u) const {
-    if (u + 1 < units_of(v, b)) return make(b, u + 1);
-    ++b;
-    while (b < v.rows && units_of(v, b) == 0) ++b;
-    return make(b, 0);
+  __device__ __forceinline__ Unit enter_row(int32_t b, int32_t u) const {
+    if (b >= v.rows) return make(v.rows, 0, 0, 0);
+    return make(b, u, sload(a->ctx + b), units_of(v, b));
   }
-  __device__ __forceinline__ Task first(int32_t b, int32_t u) const {
+  // First unit of the worker, from its schedule start (clamped).
+  __device__ __forceinline__ Unit first(int32_t b, int32_t u) const {
     b = min(max(b, 0), v.rows);
     u = max(u, 0);
     while (b < v.rows && u >= units_of(v, b)) {
       ++b;
       u = 0;
     }
-    return make(b, u);
+    return enter_row(b, u);
   }
-  __device__ __forceinline__ Task next(const Task& t) const {
-    const int32_t np = t.p + 1;
-    if (np < kPagesPerUnit && t.u * kUnit + np * kPage < max_ctx) {
-      Task n = t;
-      n.p = np;
-      return n;
-    }
-    return next_unit(t.b, t.u);
+  // Next unit after t, skipping rows that have no unit.
+  __device__ __forceinline__ Unit next(const Unit& t) const {
+    if (t.u + 1 < t.units) return make(t.b, t.u + 1, t.len, t.units);
+    int32_t b = t.b + 1;
+    while (b < v.rows && units_of(v, b) == 0) ++b;
+    return enter_row(b, 0);
   }
-  __device__ __forceinline__ bool valid(const Task& t) const { return t.b < v.rows; }
 };
 
-__device__ __forceinline__ int32_t page_token0(const Task& t) { return t.u * kUnit + t.p * kPage; }
-
-// Does the page hold K data that some query row scores?
-__device__ __forceinline__ bool has_data(const Task& t, const LogitsArgs& a) {
-  return page_token0(t) < min(t.len, a.max_ctx) &&
-         (t.u * kPagesPerUnit + t.p) < a.bt_stride;
-}
-
-__device__ __forceinline__ const uint8_t* page_ptr(const Task& t, const LogitsArgs& a,
-                                                   int page_bytes) {
-  const int32_t idx = t.u * kPagesPerUnit + t.p;
-  int64_t pid = sload(a.bt + (int64_t)t.b * a.bt_stride + idx);
-  pid = pid < 0 ? 0 : (pid >= a.num_pages ? a.num_pages - 1 : pid);
-  return a.kv + pid * (int64_t)page_bytes;
+// Does page p of unit t hold K data that some query row scores?  (Token
+// start below min(len, max_ctx), entry inside the block table.)
+__device__ __forceinline__ bool page_has_data(const Unit& t, int p, const LogitsArgs& a,
+                                              int32_t rows) {
+  const int32_t idx = t.u * kPagesPerUnit + p;
+  return t.b < rows && idx * kPage < min(t.len, a.max_ctx) && idx < a.bt_stride;
 }
 
 // Reduce four per-lane partial sums (token group tg = 0..3 of lane-group
@@ -173,50 +188,6 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   return __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
 }
 
-// Tail fill: -inf over the 256-column chunks at or past each row's unit
-// count, split evenly over all workers.
-__device__ __forceinline__ void fill_tail(const LogitsArgs& a, const SchedView& v, int next_n,
-                                          int32_t wid, int lane) {
-  const int32_t cm = v.cap;
-  const int64_t rows = (int64_t)a.batch * next_n;
-  const int64_t total = rows * cm;
-  int64_t idx = ((int64_t)wid * total) / a.num_workers;
-  const int64_t hi = ((int64_t)(wid + 1) * total) / a.num_workers;
-  if (idx >= hi) return;
-  int64_t r = idx / cm;
-  int32_t k = (int32_t)(idx - r * cm);
-  const float ninf = -__builtin_inff();
-  const v4f nv = {ninf, ninf, ninf, ninf};
-  while (idx < hi) {
-    const int32_t b = (int32_t)(r / next_n);
-    const int32_t c = b < v.rows ? units_of(v, b) : 0;
-    if (k < c) {  // chunk written by the unit pass: jump past the row's units
-      const int64_t skip = min((int64_t)(c - k), hi - idx);
-      idx += skip;
-      k += (int32_t)skip;
-    } else {
-      const int32_t col = k * kUnit + 4 * lane;
-      float* dst = a.out + r * a.ldo + col;
-      if (col + 4 <= a.max_ctx) {
-        __builtin_nontemporal_store(nv, reinterpret_cast<v4f*>(dst));
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (col + e < a.max_ctx) dst[e] = ninf;
-      }
-      ++idx;
-      ++k;
-    }
-    if (k >= cm) {
-      ++r;
-      k = 0;
-    }
-  }
-}
-
-}  // namespace pmqa
-
-namespace pmqa {
-
 // Element-format policies -------------------------------------------------
 
 // fp8: E4M3 q and K, per-token fp32 K scale applied in the epilogue.
@@ -231,16 +202,16 @@ struct Fp8Format {
   struct QFrag {
     v8i q[NN][4];
   };
-  __device__ __forceinline__ static void load_k(const uint8_t* pg, int lane, KFrag& f) {
+  __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
     const int c = lane >> 4, tl = lane & 15;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      const v4i* src = reinterpret_cast<const v4i*>(pg + (16 * tg + tl) * kHeadDim + 32 * c);
-      const v4i lo = src[0];
-      const v4i hi = src[1];
+      const int off = (16 * tg + tl) * kHeadDim + 32 * c;
+      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(pg, off, 0, 0);
+      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(pg, off + 16, 0, 0);
       f.k[tg] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    f.s = reinterpret_cast<const float*>(pg + kPage * kHeadDim)[lane];
+    f.s = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(pg, kPage * kHeadDim + 4 * lane, 0, 0));
   }
   template <int NN>
   __device__ __forceinline__ static void load_q(const LogitsArgs& a, int32_t b, int lane,
@@ -280,13 +251,14 @@ struct Fp4Format {
     v4i q[NN][4];
     int32_t sc[NN][4];
   };
-  __device__ __forceinline__ static void load_k(const uint8_t* pg, int lane, KFrag& f) {
+  __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
     const int c = lane >> 4, tl = lane & 15;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const int tok = 16 * tg + tl;
-      f.k[tg] = *reinterpret_cast<const v4i*>(pg + tok * (kHeadDim / 2) + 16 * c);
-      f.sc[tg] = pg[kPage * kHeadDim / 2 + tok * (kHeadDim / 32) + c];
+      f.k[tg] = __builtin_amdgcn_raw_buffer_load_b128(pg, tok * (kHeadDim / 2) + 16 * c, 0, 0);
+      f.sc[tg] = __builtin_amdgcn_raw_buffer_load_b8(
+          pg, kPage * kHeadDim / 2 + tok * (kHeadDim / 32) + c, 0, 0);
     }
   }
   template <int NN>
@@ -337,19 +309,29 @@ __device__ __forceinline__ void load_row(const LogitsArgs& a, int32_t b, int lan
   rs.b = b;
 }
 
-// Contract one page against every query row of the batch row, apply the
-// epilogue and store the page's 64 columns of each output row.
+template <class Fmt>
+__device__ __forceinline__ void load_page(const LogitsArgs& a, const Unit& t, int p, int32_t rows,
+                                          int lane, typename Fmt::KFrag& f) {
+  const bool ok = page_has_data(t, p, a, rows);
+  int64_t pid = t.raw[p];
+  pid = pid < 0 ? 0 : (pid >= a.num_pages ? a.num_pages - 1 : pid);
+  const uint8_t* base = a.kv + (ok ? pid : 0) * Fmt::kPageBytes;
+  Fmt::load_k(make_rsrc(base, ok ? Fmt::kPageBytes : 0), lane, f);
+}
+
+// Contract page p of unit t against every query row of the batch row and
+// apply the epilogue; lane l returns the logit of token l of the page for
+// each query row (-inf past the row's causal limit).
 template <class Fmt, int NN>
-__device__ __forceinline__ void process_page(const Task& t, const typename Fmt::KFrag& f,
-                                             RowState<Fmt, NN>& rs, const LogitsArgs& a,
-                                             int lane) {
-  if (t.b != rs.b) load_row<Fmt, NN>(a, t.b, lane, rs);
-  const int32_t tok = page_token0(t) + lane;
+__device__ __forceinline__ void process_page(const Unit& t, int p, const typename Fmt::KFrag& f,
+                                             const RowState<Fmt, NN>& rs, const LogitsArgs& a,
+                                             int32_t rows, int lane, float (&res)[NN]) {
+  const int32_t tok = t.u * kUnit + p * kPage + lane;
   const float ninf = -__builtin_inff();
   float val[NN];
 #pragma unroll
   for (int j = 0; j < NN; ++j) val[j] = ninf;
-  if (has_data(t, a)) {
+  if (page_has_data(t, p, a, rows)) {
     const int tl = lane & 15;
     uint64_t neg = 0;
     if constexpr (Fmt::kTokenScale) neg = __ballot(f.s < 0.f);
@@ -357,16 +339,20 @@ __device__ __forceinline__ void process_page(const Task& t, const typename Fmt::
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const float bnd = ((neg >> (16 * tg + tl)) & 1) ? ninf : __builtin_inff();
+      v4f acc[NN][4];
+#pragma unroll
+      for (int j = 0; j < NN; ++j)
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) acc[j][hg] = Fmt::template mma<NN>(rs.q, j, hg, f, tg);
 #pragma unroll
       for (int j = 0; j < NN; ++j) {
         float sum = 0.f;
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-          const v4f acc = Fmt::template mma<NN>(rs.q, j, hg, f, tg);
+        for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sum = __builtin_fmaf(rs.w[j][hg][i], __builtin_amdgcn_fmed3f(acc[i], 0.f, bnd), sum);
-        }
+            sum = __builtin_fmaf(rs.w[j][hg][i], __builtin_amdgcn_fmed3f(acc[j][hg][i], 0.f, bnd),
+                                 sum);
         part[j][tg] = sum;
       }
     }
@@ -377,14 +363,8 @@ __device__ __forceinline__ void process_page(const Task& t, const typename Fmt::
       val[j] = tot;
     }
   }
-  if (tok < a.max_ctx) {
 #pragma unroll
-    for (int j = 0; j < NN; ++j) {
-      const int32_t lim = t.len - NN + 1 + j;
-      const int64_t r = (int64_t)t.b * NN + j;
-      a.out[r * a.ldo + tok] = tok < lim ? val[j] : ninf;
-    }
-  }
+  for (int j = 0; j < NN; ++j) res[j] = tok < t.len - NN + 1 + j ? val[j] : ninf;
 }
 
 __device__ __forceinline__ int32_t xcd_block(int32_t bid, int32_t nblk) {
@@ -395,39 +375,100 @@ __device__ __forceinline__ int32_t xcd_block(int32_t bid, int32_t nblk) {
   return (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
 }
 
+// Staging of finished logits: every worker keeps the results of its last
+// kStageUnits<NN> units in LDS (256 floats per unit and query row) and writes
+// them out together, 16 bytes per lane, when the stage is full and at the
+// end.  Writing in a few large bursts instead of 256 bytes after every page
+// keeps most of the output traffic out of the read stream.
+template <int NN>
+struct Stage {
+  static constexpr int kUnits = 32 / NN;
+  static constexpr int kFloats = kUnits * NN * kUnit;
+};
+
+template <int NN>
+__device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* stage,
+                                            const int32_t* meta, int32_t n, int lane) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = meta[2 * i];
+    const int32_t u = meta[2 * i + 1];
+    const int32_t col = u * kUnit + 4 * lane;
+#pragma unroll
+    for (int j = 0; j < NN; ++j) {
+      const int64_t r = (int64_t)b * NN + j;
+      const v4f v = *reinterpret_cast<const v4f*>(stage + (i * NN + j) * kUnit + 4 * lane);
+      const rsrc_t orow = make_rsrc(a.out + r * a.ldo, a.max_ctx * 4);
+      if (u * kUnit + kUnit <= a.max_ctx) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), orow, 4 * col, 0, 0);
+      } else {  // unit crosses max_ctx: per-column stores, the rest is dropped
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[e]), orow, 4 * (col + e), 0, 0);
+      }
+    }
+  }
+}
+
 template <class Fmt, int NN>
-__global__ __launch_bounds__(kBlockThreads) void logits_kernel(const LogitsArgs a) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void logits_kernel(const LogitsArgs a) {
+  __shared__ float stage_all[kWavesPerBlock][Stage<NN>::kFloats];
+  __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<NN>::kUnits];
   const int lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wid = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
   if (wid >= a.num_workers) return;
   const SchedView v = make_view(a);
-  if (v.rows > 0) {
-    Iter it;
-    it.v = v;
-    it.ctx = a.ctx;
-    it.end_b = sload(v.starts + 2 * wid + 2);
-    it.end_u = sload(v.starts + 2 * wid + 3);
-    it.max_ctx = a.max_ctx;
-    Task cur = it.first(sload(v.starts + 2 * wid), sload(v.starts + 2 * wid + 1));
-    typename Fmt::KFrag fa, fb;
-    RowState<Fmt, NN> rs;
-    rs.b = -1;
-    if (it.valid(cur) && has_data(cur, a))
-      Fmt::load_k(page_ptr(cur, a, Fmt::kPageBytes), lane, fa);
-    while (it.valid(cur)) {
-      const Task nx = it.next(cur);
-      if (it.valid(nx) && has_data(nx, a))
-        Fmt::load_k(page_ptr(nx, a, Fmt::kPageBytes), lane, fb);
-      process_page<Fmt, NN>(cur, fa, rs, a, lane);
-      if (!it.valid(nx)) break;
-      cur = it.next(nx);
-      if (it.valid(cur) && has_data(cur, a))
-        Fmt::load_k(page_ptr(cur, a, Fmt::kPageBytes), lane, fa);
-      process_page<Fmt, NN>(nx, fb, rs, a, lane);
+  if (v.rows == 0) return;
+  float* stage = stage_all[wave];
+  int32_t* meta = meta_all[wave];
+  Iter it;
+  it.v = v;
+  it.a = &a;
+  it.end_b = sload(v.starts + 2 * wid + 2);
+  it.end_u = sload(v.starts + 2 * wid + 3);
+  Unit cur = it.first(sload(v.starts + 2 * wid), sload(v.starts + 2 * wid + 1));
+  if (!it.valid(cur)) return;
+  const int32_t rows = v.rows;
+  // K ring: page p of a unit always lives in slot p, so the 4 pages of the
+  // next unit are in flight while the current one is consumed.
+  typename Fmt::KFrag ring[kPagesPerUnit];
+  RowState<Fmt, NN> rs;
+  rs.b = -1;
+#pragma unroll
+  for (int p = 0; p < kPagesPerUnit; ++p) load_page<Fmt>(a, cur, p, rows, lane, ring[p]);
+  int32_t staged = 0;
+  while (true) {
+    if (cur.b != rs.b) {  // new batch row: its query block and weights
+      load_row<Fmt, NN>(a, cur.b, lane, rs);
+      __builtin_amdgcn_s_waitcnt(0);
     }
+    const Unit nxt = it.next(cur);  // lookahead: same iterator as the consumer
+    float* dst = stage + staged * NN * kUnit;
+#pragma unroll
+    for (int p = 0; p < kPagesPerUnit; ++p) {
+      float res[NN];
+      process_page<Fmt, NN>(cur, p, ring[p], rs, a, rows, lane, res);
+      load_page<Fmt>(a, nxt, p, rows, lane, ring[p]);
+#pragma unroll
+      for (int j = 0; j < NN; ++j) dst[j * kUnit + p * kPage + lane] = res[j];
+    }
+    if (lane == 0) {
+      meta[2 * staged] = cur.b;
+      meta[2 * staged + 1] = cur.u;
+    }
+    ++staged;
+    const bool last = !it.valid(nxt);
+    if (staged == Stage<NN>::kUnits || last) {
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      flush_stage<NN>(a, stage, meta, staged, lane);
+      __builtin_amdgcn_wave_barrier();
+      staged = 0;
+    }
+    if (last) break;
+    cur = nxt;
   }
-  fill_tail(a, v, NN, wid, lane);
 }
 
 template <class Fmt>

@@ -10,11 +10,14 @@
 // One workgroup of 1024 threads:
 //   1. thread i owns a contiguous slice of rows and sums their unit counts
 //      c_b = ceil(ctx_b / 256) (negative lengths count as 0);
-//   2. a block-wide exclusive scan of the slice sums gives each slice's base;
-//      the threads write the row prefix sums S[0..B] to the schedule buffer;
+//   2. a block-wide exclusive scan of the slice sums (shuffles within each
+//      wavefront, then the 16 wavefront totals) gives each slice's base; the
+//      threads write the row prefix sums S[0..B] to the schedule buffer and,
+//      for up to 12288 rows, to LDS;
 //   3. after a barrier every worker w = 0..W takes g = floor(w*T/W) and finds
-//      its row as upper_bound(S, g) - 1 by binary search, which can never land
-//      on a row with zero units (S[b] <= g < S[b+1] implies c_b > 0).
+//      its row as upper_bound(S, g) - 1 by binary search (in LDS when the
+//      prefix sums fit there), which can never land on a row with zero units
+//      (S[b] <= g < S[b+1] implies c_b > 0).
 #include <hip/hip_runtime.h>
 
 #include "pmqa_internal.h"
@@ -24,44 +27,78 @@ namespace pmqa {
 namespace {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kWaves = kSchedThreads / 64;
+constexpr int kLdsPrefix = 12288;  // rows whose prefix sums are searched in LDS
 
 __device__ inline int32_t units_of_len(int32_t len) {
   return len > 0 ? (int32_t)(((int64_t)len + kUnit - 1) / kUnit) : 0;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ inline int64_t wave_inclusive_scan(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// First index i in [0, n) with P[i] > g (n if none); P is non-decreasing.
+template <class T>
+__device__ inline int32_t upper_bound(const T* P, int32_t n, int64_t g) {
+  int32_t a = 0;
+  while (n > 0) {
+    const int32_t half = n >> 1;
+    if ((int64_t)P[a + half] <= g) {
+      a += half + 1;
+      n -= half + 1;
+    } else {
+      n = half;
+    }
+  }
+  return a;
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ ctx,
                                                                  int32_t batch, int32_t workers,
                                                                  int32_t* __restrict__ sched) {
-  __shared__ int64_t scan[kSchedThreads];
+  __shared__ int64_t wave_sums[kWaves];
+  __shared__ int32_t Sl[kLdsPrefix + 1];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   int32_t* starts = sched + kSchedHeader;
   int32_t* S = starts + 2 * (workers + 1);
+  const bool in_lds = batch <= kLdsPrefix;
 
+  // 1. Each thread owns a contiguous slice of rows; sum their unit counts.
   const int32_t chunk = (batch + kSchedThreads - 1) / kSchedThreads;
   const int32_t lo = min(batch, tid * chunk);
   const int32_t hi = min(batch, lo + chunk);
   int64_t local = 0;
   for (int32_t b = lo; b < hi; ++b) local += units_of_len(ctx[b]);
 
-  // Hillis-Steele inclusive scan over the 1024 slice sums.
-  scan[tid] = local;
+  // 2. Block-wide exclusive scan: within each wave, then across waves.
+  const int64_t incl = wave_inclusive_scan(local);
+  if (lane == 63) wave_sums[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    int64_t v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  int64_t wave_base = 0, total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int64_t v = wave_sums[w];
+    wave_base += w < wave ? v : 0;
+    total += v;
   }
-  const int64_t total = scan[kSchedThreads - 1];
   const bool fits = total <= (int64_t)INT32_MAX;
-
-  int64_t run = scan[tid] - local;  // exclusive base of this slice
+  int64_t run = wave_base + incl - local;
   for (int32_t b = lo; b < hi; ++b) {
     S[b] = (int32_t)run;
+    if (in_lds) Sl[b] = (int32_t)run;
     run += units_of_len(ctx[b]);
   }
   if (tid == 0) {
     S[batch] = (int32_t)total;
+    if (in_lds) Sl[batch] = (int32_t)total;
     sched[0] = kSchedMagic;
     sched[1] = batch;
     sched[2] = workers;
@@ -75,27 +112,19 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   __threadfence_block();
   __syncthreads();
 
+  // 3. Worker w starts at global unit floor(w*T/W): its row is the last b
+  //    with S[b] <= g, found by binary search (never a row without units).
   for (int32_t w = tid; w <= workers; w += kSchedThreads) {
     int32_t row = batch, unit = 0;
     if (fits && w < workers) {
       const int64_t g = ((int64_t)w * total) / workers;
-      // first index i in [0, batch] with S[i] > g
-      int32_t a = 0, n = batch + 1;
-      while (n > 0) {
-        const int32_t half = n >> 1;
-        if ((int64_t)S[a + half] <= g) {
-          a += half + 1;
-          n -= half + 1;
-        } else {
-          n = half;
-        }
-      }
+      const int32_t a = in_lds ? upper_bound(Sl, batch + 1, g) : upper_bound(S, batch + 1, g);
       row = a - 1;
       if (row >= batch) {  // g == total: nothing left for this worker
         row = batch;
         unit = 0;
       } else {
-        unit = (int32_t)(g - S[row]);
+        unit = (int32_t)(g - (in_lds ? Sl[row] : S[row]));
       }
     }
     starts[2 * w] = row;
