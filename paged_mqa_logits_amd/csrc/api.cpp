@@ -206,12 +206,12 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
   a.bt_stride = s.bt_stride;
   a.max_ctx = s.max_ctx;
   a.num_workers = s.workers;
-  hipError_t e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
-                                             : pmqa::launch_logits_fp4(a, s.next_n, stream);
+  hipError_t e = pmqa::launch_neg_inf_fill(logits, s.ldo, (int64_t)s.batch * s.next_n, s.max_ctx,
+                                           g_cus[dev].load(std::memory_order_acquire), stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "-inf fill launch: %s", hipGetErrorString(e));
+  e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
+                                  : pmqa::launch_logits_fp4(a, s.next_n, stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
-  e = pmqa::launch_tail_fill(logits, s.ldo, s.batch, s.next_n, s.max_ctx, sched, s.workers,
-                             g_cus[dev].load(std::memory_order_acquire), stream);
-  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "tail fill launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -44,8 +44,9 @@
 // lookahead and the consumer walk the same iterator, so they always agree on
 // which (row, unit) comes next, including across skipped zero-length rows.
 //
-// Columns past each row's last unit are written with -inf by a separate
-// kernel (tail_fill.hip) launched right after this one.
+// Every output column is first set to -inf by a separate kernel
+// (tail_fill.hip) launched right before this one; this kernel overwrites the
+// columns of the units it processes.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -43,10 +43,10 @@ hipError_t launch_schedule(const int32_t* ctx, int32_t batch, int32_t num_worker
                            int32_t* sched, hipStream_t stream);
 hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, hipStream_t stream);
 hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream);
-// -inf over the columns of each row past its last scheduled unit.
-hipError_t launch_tail_fill(float* out, int64_t ldo, int32_t batch, int32_t next_n,
-                            int32_t max_ctx, const int32_t* sched, int32_t workers, int32_t blocks,
-                            hipStream_t stream);
+// -inf over columns [0, max_ctx) of every output row (runs before the unit
+// kernel, which overwrites the scheduled units).
+hipError_t launch_neg_inf_fill(float* out, int64_t ldo, int64_t rows, int32_t max_ctx,
+                               int32_t blocks, hipStream_t stream);
 
 // Resident workgroups per compute unit of a logits kernel (occupancy query).
 hipError_t logits_blocks_per_cu(int variant, int next_n, int* blocks);
