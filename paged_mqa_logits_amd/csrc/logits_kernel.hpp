@@ -66,6 +66,8 @@ constexpr int kFmtFp4 = 4;      // cbsz/blgp code of E2M1 operands
 constexpr int kScaleOne = 127;  // E8M0 encoding of 1.0
 // Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy bits of a streaming (non-temporal) buffer load.
+constexpr int kLoadNT = 2;
 
 // Wave-uniform read of read-only metadata (schedule, context lengths, block
 // table) through the constant address space, so it is a scalar load that
@@ -192,27 +194,59 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
 // Element-format policies -------------------------------------------------
 
 // fp8: E4M3 q and K, per-token fp32 K scale applied in the epilogue.
+//
+// A page's 8 KB of K values are read with contiguous, non-temporal 16-byte
+// loads (each load instruction covers 1 KB: eight full 128-byte lines of 8
+// tokens), which streams faster from HBM than loading straight in MFMA
+// operand order (16 half-lines per instruction).  Before the page is
+// contracted it is passed through the wave's 8 KB LDS buffer to reach the
+// operand layout.  In LDS, 16-byte chunk k of token t sits at
+// t*128 + ((k ^ ((t >> 1) & 7)) << 4): the 1 KB written by each store
+// instruction stays contiguous, and the 16 lanes of each operand read hit 16
+// distinct bank groups.
 struct Fp8Format {
   static constexpr int kPageBytes = kFp8PageBytes;
   static constexpr bool kTokenScale = true;
+  static constexpr int kLdsBytes = kPage * kHeadDim;  // transpose buffer per wave
   struct KFrag {
-    v8i k[4];
-    float s;  // scale of token `lane` of the page
+    v4i raw[8];  // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
+    float s;     // scale of token `lane` of the page
+  };
+  struct KOp {
+    v8i k[4];    // MFMA B operand of token group tg
   };
   template <int NN>
   struct QFrag {
     v8i q[NN][4];
   };
   __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
-    const int c = lane >> 4, tl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      f.raw[i] = __builtin_amdgcn_raw_buffer_load_b128(pg, 1024 * i + 16 * lane, 0, kLoadNT);
+    f.s = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(pg, kPage * kHeadDim + 4 * lane, 0, 0));
+  }
+  // Reorder a page into operand layout through the wave's LDS buffer.
+  __device__ __forceinline__ static void to_operands(const KFrag& f, uint8_t* lds, int lane,
+                                                     KOp& o) {
+    // store i writes tokens 8i + (lane >> 3), chunk lane & 7; the swizzle of
+    // token t = 8i + (lane >> 3) is (4i + (lane >> 4)) & 7
+    const int tok_in = lane >> 3;
+    const int w_even = tok_in * 128 + (((lane & 7) ^ ((lane >> 4) & 7)) << 4);
+    const int w_odd = tok_in * 128 + (((lane & 7) ^ ((4 + (lane >> 4)) & 7)) << 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<v4i*>(lds + 1024 * i + ((i & 1) ? w_odd : w_even)) = f.raw[i];
+    // operand lane (tl, c) of group tg wants token 16 tg + tl, chunks 2c, 2c+1
+    const int tl = lane & 15, c = lane >> 4;
+    const int sw = (tl >> 1) & 7;
+    const int r0 = tl * 128 + (((2 * c) ^ sw) << 4);
+    const int r1 = tl * 128 + (((2 * c + 1) ^ sw) << 4);
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      const int off = (16 * tg + tl) * kHeadDim + 32 * c;
-      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(pg, off, 0, 0);
-      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(pg, off + 16, 0, 0);
-      f.k[tg] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const v4i lo = *reinterpret_cast<const v4i*>(lds + 2048 * tg + r0);
+      const v4i hi = *reinterpret_cast<const v4i*>(lds + 2048 * tg + r1);
+      o.k[tg] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    f.s = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(pg, kPage * kHeadDim + 4 * lane, 0, 0));
   }
   template <int NN>
   __device__ __forceinline__ static void load_q(const LogitsArgs& a, int32_t b, int lane,
@@ -230,10 +264,10 @@ struct Fp8Format {
       }
   }
   template <int NN>
-  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KFrag& f,
+  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& o,
                                             int tg) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.q[j][hg], f.k[tg], zero, kFmtFp8,
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.q[j][hg], o.k[tg], zero, kFmtFp8,
                                                             kFmtFp8, 0, kScaleOne, 0, kScaleOne);
   }
 };
@@ -243,10 +277,15 @@ struct Fp8Format {
 struct Fp4Format {
   static constexpr int kPageBytes = kFp4PageBytes;
   static constexpr bool kTokenScale = false;
+  static constexpr int kLdsBytes = 0;
   struct KFrag {
     v4i k[4];
     int32_t sc[4];
   };
+  typedef KFrag KOp;  // loaded directly in operand layout
+  __device__ __forceinline__ static void to_operands(const KFrag& f, uint8_t*, int, KOp& o) {
+    o = f;
+  }
   template <int NN>
   struct QFrag {
     v4i q[NN][4];
@@ -276,7 +315,7 @@ struct Fp4Format {
       }
   }
   template <int NN>
-  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KFrag& f,
+  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& f,
                                             int tg) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const v4i x = q.q[j][hg];
@@ -325,8 +364,9 @@ __device__ __forceinline__ void load_page(const LogitsArgs& a, const Unit& t, in
 // each query row (-inf past the row's causal limit).
 template <class Fmt, int NN>
 __device__ __forceinline__ void process_page(const Unit& t, int p, const typename Fmt::KFrag& f,
-                                             const RowState<Fmt, NN>& rs, const LogitsArgs& a,
-                                             int32_t rows, int lane, float (&res)[NN]) {
+                                             uint8_t* lds, const RowState<Fmt, NN>& rs,
+                                             const LogitsArgs& a, int32_t rows, int lane,
+                                             float (&res)[NN]) {
   const int32_t tok = t.u * kUnit + p * kPage + lane;
   const float ninf = -__builtin_inff();
   float val[NN];
@@ -334,6 +374,8 @@ __device__ __forceinline__ void process_page(const Unit& t, int p, const typenam
   for (int j = 0; j < NN; ++j) val[j] = ninf;
   if (page_has_data(t, p, a, rows)) {
     const int tl = lane & 15;
+    typename Fmt::KOp op;
+    Fmt::to_operands(f, lds, lane, op);
     uint64_t neg = 0;
     if constexpr (Fmt::kTokenScale) neg = __ballot(f.s < 0.f);
     float part[NN][4];
@@ -344,7 +386,7 @@ __device__ __forceinline__ void process_page(const Unit& t, int p, const typenam
 #pragma unroll
       for (int j = 0; j < NN; ++j)
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) acc[j][hg] = Fmt::template mma<NN>(rs.q, j, hg, f, tg);
+        for (int hg = 0; hg < 4; ++hg) acc[j][hg] = Fmt::template mma<NN>(rs.q, j, hg, op, tg);
 #pragma unroll
       for (int j = 0; j < NN; ++j) {
         float sum = 0.f;
@@ -383,7 +425,7 @@ __device__ __forceinline__ int32_t xcd_block(int32_t bid, int32_t nblk) {
 // keeps most of the output traffic out of the read stream.
 template <int NN>
 struct Stage {
-  static constexpr int kUnits = 32 / NN;
+  static constexpr int kUnits = 28 / NN;
   static constexpr int kFloats = kUnits * NN * kUnit;
 };
 
@@ -415,6 +457,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(1
 void logits_kernel(const LogitsArgs a) {
   __shared__ float stage_all[kWavesPerBlock][Stage<NN>::kFloats];
   __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<NN>::kUnits];
+  __shared__ __attribute__((aligned(16))) uint8_t xpose_all[kWavesPerBlock][Fmt::kLdsBytes > 0 ? Fmt::kLdsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wid = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
@@ -423,6 +466,7 @@ void logits_kernel(const LogitsArgs a) {
   if (v.rows == 0) return;
   float* stage = stage_all[wave];
   int32_t* meta = meta_all[wave];
+  uint8_t* xpose = xpose_all[wave];
   Iter it;
   it.v = v;
   it.a = &a;
@@ -449,7 +493,7 @@ void logits_kernel(const LogitsArgs a) {
 #pragma unroll
     for (int p = 0; p < kPagesPerUnit; ++p) {
       float res[NN];
-      process_page<Fmt, NN>(cur, p, ring[p], rs, a, rows, lane, res);
+      process_page<Fmt, NN>(cur, p, ring[p], xpose, rs, a, rows, lane, res);
       load_page<Fmt>(a, nxt, p, rows, lane, ring[p]);
 #pragma unroll
       for (int j = 0; j < NN; ++j) dst[j * kUnit + p * kPage + lane] = res[j];
