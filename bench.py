@@ -48,13 +48,19 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(ctx, next_n, max_ctx, heads, dim, page, sched_bytes):
-    """Bytes the method must move for one logits call (partial pages not counted)."""
+def algorithmic_bytes(ctx, next_n, max_ctx, heads, dim, page, sched_bytes, variant="fp8"):
+    """Bytes the method must move for one logits call (partial pages not counted).
+
+    fp8: 128 E4M3 bytes + a 4-byte scale per KV token, q 128 B + weight 4 B
+    per head.  fp4: 64 packed bytes + 4 E8M0 scales per KV token, q 64 B + 4
+    scales + weight 4 B per head.  K is counted once per batch row."""
     ctx = ctx.astype(np.int64)
     B = len(ctx)
-    k_stream = (dim + 4) * int(ctx.sum())                  # e4m3 row + fp32 scale per token
+    per_tok = dim + 4 if variant == "fp8" else dim // 2 + dim // 32
+    per_head = dim + 4 if variant == "fp8" else dim // 2 + dim // 32 + 4
+    k_stream = per_tok * int(ctx.sum())
     table = 4 * int(((ctx + page - 1) // page).sum())      # block-table entries read
-    qw = B * next_n * heads * (dim + 4)                     # q bytes + fp32 weights
+    qw = B * next_n * heads * per_head                      # q (+ scales) + fp32 weights
     out = 4 * B * next_n * max_ctx                          # every logit, -inf included
     return k_stream + table + qw + 4 * B + out + sched_bytes
 
@@ -83,7 +89,7 @@ def read_traffic(expected_hash, launches_bytes):
 
 
 def cpu_baseline(data, n_rows, seed):
-    """Time the fp64 oracle on a fixed random subset of rows."""
+    """Time the fp64 oracle on a fixed random subset of batch rows."""
     from oracle import reference
     try:
         from threadpoolctl import threadpool_info
@@ -93,14 +99,35 @@ def cpu_baseline(data, n_rows, seed):
     B = len(data["context_lens"])
     rng = np.random.default_rng(seed)
     rows = np.sort(rng.choice(B, size=min(n_rows, B), replace=False))
+    nn = data["next_n"]
+    out_rows = [int(b) * nn + j for b in rows for j in range(nn)]
     t0 = time.perf_counter()
-    reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"],
-                                   data["context_lens"], data["block_table"],
-                                   data["max_context_len"], rows=rows.tolist())
+    if data["variant"] == "fp8":
+        reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"],
+                                       data["context_lens"], data["block_table"],
+                                       data["max_context_len"], rows=out_rows)
+    else:
+        reference.paged_mqa_logits_fp4(data["q"], data["q_scale"], data["kv_cache"],
+                                       data["weights"], data["context_lens"],
+                                       data["block_table"], data["max_context_len"],
+                                       rows=out_rows)
     dt = time.perf_counter() - t0
-    toks = int(data["context_lens"][rows].astype(np.int64).sum())
+    toks = scored_tokens(data["context_lens"][rows], nn, data["max_context_len"])
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{len(rows)} of {B} rows (seeded), {toks} KV tokens, {dt:.1f} s"}
+
+
+def describe(cfg):
+    if cfg.ctx_kind == "lognormal":
+        dist = (f"ctx lognormal(median {cfg.ctx_median:g}, sigma {cfg.ctx_sigma:g}) clipped "
+                f"[{cfg.ctx_lo}, {cfg.ctx_hi}]")
+    else:
+        dist = f"ctx uniform [{cfg.ctx_lo}, {cfg.ctx_hi}]"
+    zeros = f", {cfg.zero_frac:.0%} empty rows" if cfg.zero_frac else ""
+    return (f"{cfg.name}: B={cfg.batch} decode, next_n={cfg.next_n}, {cfg.variant}, 64 heads, "
+            f"head_dim 128, 64-token pages, {dist}{zeros}, logits [{cfg.batch * cfg.next_n}, "
+            f"{cfg.max_context_len}] fp32; step = graph replay of compute_schedule + "
+            f"paged_mqa_logits_{cfg.variant}")
 
 
 def main():
@@ -111,6 +138,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the workload timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="workload name (default: the B=2048 fp8 decode the metric is quoted on)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this size "
                          "(reference kernel for rocprofv3 byte counters)")
@@ -125,24 +154,35 @@ def main():
     import paged_mqa_logits_amd as pmqa
     from workloads import CONFIGS, make_workload
 
-    cfg = CONFIGS[WORKLOAD]
-    print(f"[bench] generating {WORKLOAD}", file=sys.stderr, flush=True)
-    data = make_workload(WORKLOAD)
+    cfg = CONFIGS[args.workload]
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    data = make_workload(args.workload)
+    fp8 = data["variant"] == "fp8"
+    variant = pmqa.VARIANT_FP8 if fp8 else pmqa.VARIANT_FP4
     ctx_np = data["context_lens"]
     M = data["max_context_len"]
     NN = data["next_n"]
     B = len(ctx_np)
     torch.cuda.set_device(0)
-    dev = {k: torch.from_numpy(np.ascontiguousarray(data[k])).cuda()
-           for k in ("q", "kv_cache", "weights", "context_lens", "block_table")}
-    W = pmqa.default_num_workers(pmqa.VARIANT_FP8, NN)
+    keys = ("q", "kv_cache", "weights", "context_lens", "block_table") + (() if fp8 else ("q_scale",))
+    dev = {k: torch.from_numpy(np.ascontiguousarray(data[k])).cuda() for k in keys}
+    W = pmqa.default_num_workers(variant, NN)
     sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
     out = torch.empty((B * NN, M), dtype=torch.float32, device="cuda")
 
+    def logits_call():
+        if fp8:
+            pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                      dev["context_lens"], dev["block_table"], sched, M, out=out,
+                                      num_workers=W)
+        else:
+            pmqa.paged_mqa_logits_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
+                                      dev["context_lens"], dev["block_table"], sched, M, out=out,
+                                      num_workers=W)
+
     def step():
         pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
-        pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], dev["context_lens"],
-                                  dev["block_table"], sched, M, out=out, num_workers=W)
+        logits_call()
 
     step()
     torch.cuda.synchronize()
@@ -174,8 +214,7 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
     for i in range(args.steps):
         ev[2 * i].record(stream)
-        pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], dev["context_lens"],
-                                  dev["block_table"], sched, M, out=out, num_workers=W)
+        logits_call()
         ev[2 * i + 1].record(stream)
     torch.cuda.synchronize()
     k_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)])
@@ -200,9 +239,15 @@ def main():
 
     # sampled parity of the last output against the oracle
     from oracle import reference
-    rows = [int(np.argmax(ctx_np)), int(np.nonzero(ctx_np == 0)[0][0]) if (ctx_np == 0).any() else 0, 1, B - 1]
-    ref = reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"], ctx_np,
-                                         data["block_table"], M, rows=rows, want_tol=True)
+    bs = [int(np.argmax(ctx_np)), int(np.nonzero(ctx_np == 0)[0][0]) if (ctx_np == 0).any() else 0, 1, B - 1]
+    rows = [b * NN + j for b in bs for j in range(NN)]
+    if fp8:
+        ref = reference.paged_mqa_logits_fp8(data["q"], data["kv_cache"], data["weights"], ctx_np,
+                                             data["block_table"], M, rows=rows, want_tol=True)
+    else:
+        ref = reference.paged_mqa_logits_fp4(data["q"], data["q_scale"], data["kv_cache"],
+                                             data["weights"], ctx_np, data["block_table"], M,
+                                             rows=rows, want_tol=True)
     got = out[rows].cpu().numpy()
     masked = np.isneginf(ref["logits"])
     ok = bool(np.all(got.view(np.uint32)[masked] == np.uint32(0xFF800000)) and
@@ -210,10 +255,11 @@ def main():
 
     tokens = scored_tokens(ctx_np, NN, M)
     sbytes = pmqa.schedule_bytes(B, W)
-    alg = algorithmic_bytes(ctx_np, NN, M, pmqa.NUM_HEADS, pmqa.HEAD_DIM, pmqa.PAGE_SIZE, sbytes)
+    alg = algorithmic_bytes(ctx_np, NN, M, pmqa.NUM_HEADS, pmqa.HEAD_DIM, pmqa.PAGE_SIZE, sbytes,
+                            data["variant"])
     achieved = alg / (k_mean * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_traffic(src_hash, alg)
+    traffic = read_traffic(src_hash, alg) if args.workload == WORKLOAD else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -231,13 +277,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": data["variant"],
         "data": "synthetic",
         "config": {
-            "workload": ("large_fp8: B=2048 decode, next_n=1, 64 heads, head_dim 128, 64-token "
-                         "pages, ctx lognormal(median 4096, sigma 1) clipped [1, 65536], 10% "
-                         "empty rows, logits [2048, 65536] fp32; step = graph replay of "
-                         "compute_schedule + paged_mqa_logits_fp8"),
+            "workload": describe(cfg),
             "batch": B, "next_n": NN, "max_context_len": M, "kv_tokens_per_step": tokens,
             "num_workers": W, "graph": True,
         },
@@ -248,7 +291,8 @@ def main():
         "schedule_kernel_us": s_mean * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "paged_mqa_logits_fp8 = neg_inf_fill_kernel + logits_kernel<Fp8Format, 1>",
+                     "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
+                                f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}>"),
                      "kernel_source_hash": src_hash},
         "sampled_parity": ok,
         "cpu_baseline": cpu,

@@ -274,31 +274,52 @@ struct Fp8Format {
 
 // MXFP4: E2M1 q and K with one E8M0 scale per 32 elements, fed to the MFMA
 // as per-lane block scales; no per-token scale.
+//
+// As for fp8, a page's 4 KB of packed values are read with contiguous
+// non-temporal 16-byte loads (1 KB, i.e. 16 tokens, per instruction) and
+// reordered to operand layout through the wave's LDS buffer: chunk k (16
+// bytes = 32 elements) of token t sits at t*64 + ((k ^ ((t >> 2) & 3)) << 4),
+// which keeps stores and operand reads free of bank conflicts.  Lane l also
+// loads the four block scales of token l, and each operand lane fetches the
+// scale it needs from the owning lane with ds_bpermute.
 struct Fp4Format {
   static constexpr int kPageBytes = kFp4PageBytes;
   static constexpr bool kTokenScale = false;
-  static constexpr int kLdsBytes = 0;
+  static constexpr int kLdsBytes = kPage * kHeadDim / 2;  // transpose buffer per wave
   struct KFrag {
-    v4i k[4];
+    v4i raw[4];   // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
+    int32_t sc;   // the 4 E8M0 block scales of token `lane`
+  };
+  struct KOp {
+    v4i k[4];     // B operand of token group tg (16 bytes = 32 elements)
     int32_t sc[4];
   };
-  typedef KFrag KOp;  // loaded directly in operand layout
-  __device__ __forceinline__ static void to_operands(const KFrag& f, uint8_t*, int, KOp& o) {
-    o = f;
-  }
   template <int NN>
   struct QFrag {
     v4i q[NN][4];
     int32_t sc[NN][4];
   };
   __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
-    const int c = lane >> 4, tl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.raw[i] = __builtin_amdgcn_raw_buffer_load_b128(pg, 1024 * i + 16 * lane, 0, kLoadNT);
+    f.sc = __builtin_amdgcn_raw_buffer_load_b32(pg, kPage * kHeadDim / 2 + 4 * lane, 0, 0);
+  }
+  __device__ __forceinline__ static void to_operands(const KFrag& f, uint8_t* lds, int lane,
+                                                     KOp& o) {
+    // store i writes token 16 i + (lane >> 2), chunk lane & 3; its swizzle is
+    // (lane >> 4) & 3
+    const int w = (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(lds + 1024 * i + w) = f.raw[i];
+    // operand lane (tl, c) of group tg wants token 16 tg + tl, chunk c
+    const int tl = lane & 15, c = lane >> 4;
+    const int r = tl * 64 + ((c ^ ((tl >> 2) & 3)) << 4);
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      const int tok = 16 * tg + tl;
-      f.k[tg] = __builtin_amdgcn_raw_buffer_load_b128(pg, tok * (kHeadDim / 2) + 16 * c, 0, 0);
-      f.sc[tg] = __builtin_amdgcn_raw_buffer_load_b8(
-          pg, kPage * kHeadDim / 2 + tok * (kHeadDim / 32) + c, 0, 0);
+      o.k[tg] = *reinterpret_cast<const v4i*>(lds + 1024 * tg + r);
+      const int owner = __builtin_amdgcn_ds_bpermute(4 * (16 * tg + tl), f.sc);
+      o.sc[tg] = (owner >> (8 * c)) & 0xFF;
     }
   }
   template <int NN>
@@ -315,15 +336,15 @@ struct Fp4Format {
       }
   }
   template <int NN>
-  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& f,
+  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& o,
                                             int tg) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const v4i x = q.q[j][hg];
-    const v4i y = f.k[tg];
+    const v4i y = o.k[tg];
     const v8i a8 = {x[0], x[1], x[2], x[3], 0, 0, 0, 0};
     const v8i b8 = {y[0], y[1], y[2], y[3], 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, kFmtFp4, kFmtFp4, 0,
-                                                            q.sc[j][hg], 0, f.sc[tg]);
+                                                            q.sc[j][hg], 0, o.sc[tg]);
   }
 };
 
