@@ -20,7 +20,11 @@ SOURCES = ["api.cpp", "schedule.hip", "logits_fp8.hip", "logits_fp4.hip", "tail_
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
-DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results go straight to VGPRs: with one wave per SIMD the register
+# budget exceeds 256, where the compiler would otherwise pick the AGPR form
+# and copy every accumulator back with v_accvgpr_read.
+DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc():

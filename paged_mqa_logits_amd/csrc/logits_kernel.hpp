@@ -208,6 +208,10 @@ struct Fp8Format {
   static constexpr int kPageBytes = kFp8PageBytes;
   static constexpr bool kTokenScale = true;
   static constexpr int kLdsBytes = kPage * kHeadDim;  // transpose buffer per wave
+  // Waves per SIMD (one: the stream is memory-bound and the registers go to
+  // the K ring) and units of logits staged per wave.
+  static constexpr int waves_per_simd(int) { return 1; }
+  static constexpr int stage_units(int nn) { return 28 / nn; }
   struct KFrag {
     v4i raw[8];  // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
     float s;     // scale of token `lane` of the page
@@ -286,6 +290,11 @@ struct Fp4Format {
   static constexpr int kPageBytes = kFp4PageBytes;
   static constexpr bool kTokenScale = false;
   static constexpr int kLdsBytes = kPage * kHeadDim / 2;  // transpose buffer per wave
+  // Two waves per SIMD (a page costs as many MFMA and VALU issues as an fp8
+  // page for half the bytes, so a second wave fills the issue gaps of the
+  // first), with the logits stage halved to fit two workgroups in LDS.
+  static constexpr int waves_per_simd(int) { return 2; }
+  static constexpr int stage_units(int nn) { return 14 / nn; }
   struct KFrag {
     v4i raw[4];   // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
     int32_t sc;   // the 4 E8M0 block scales of token `lane`
@@ -399,10 +408,17 @@ __device__ __forceinline__ void process_page(const Unit& t, int p, const typenam
     Fmt::to_operands(f, lds, lane, op);
     uint64_t neg = 0;
     if constexpr (Fmt::kTokenScale) neg = __ballot(f.s < 0.f);
+    // Upper clamp of the ReLU: +inf, or -inf for a token whose scale is
+    // negative (ReLU(s*x) = s*min(x, 0) then, the scale being applied after
+    // the head sum).  Kept opaque when it is a constant so the ReLU stays one
+    // med3 instead of a max that the compiler precedes with a NaN-quieting
+    // max(x, x).
+    float pos = __builtin_inff();
+    if constexpr (!Fmt::kTokenScale) __asm__("" : "+v"(pos));
     float part[NN][4];
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      const float bnd = ((neg >> (16 * tg + tl)) & 1) ? ninf : __builtin_inff();
+      const float bnd = ((neg >> (16 * tg + tl)) & 1) ? ninf : pos;
       v4f acc[NN][4];
 #pragma unroll
       for (int j = 0; j < NN; ++j)
@@ -440,13 +456,14 @@ __device__ __forceinline__ int32_t xcd_block(int32_t bid, int32_t nblk) {
 }
 
 // Staging of finished logits: every worker keeps the results of its last
-// kStageUnits<NN> units in LDS (256 floats per unit and query row) and writes
-// them out together, 16 bytes per lane, when the stage is full and at the
-// end.  Writing in a few large bursts instead of 256 bytes after every page
-// keeps most of the output traffic out of the read stream.
-template <int NN>
+// kUnits units in LDS (256 floats per unit and query row) and writes them
+// out together, 16 bytes per lane, when the stage is full and at the end.
+// Writing in a few large bursts instead of 256 bytes after every page keeps
+// most of the output traffic out of the read stream.  The stage takes what
+// LDS is left once the format's workgroups per compute unit are resident.
+template <class Fmt, int NN>
 struct Stage {
-  static constexpr int kUnits = 28 / NN;
+  static constexpr int kUnits = Fmt::stage_units(NN);
   static constexpr int kFloats = kUnits * NN * kUnit;
 };
 
@@ -454,8 +471,8 @@ template <int NN>
 __device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* stage,
                                             const int32_t* meta, int32_t n, int lane) {
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t b = meta[2 * i];
-    const int32_t u = meta[2 * i + 1];
+    const int32_t b = __builtin_amdgcn_readfirstlane(meta[2 * i]);
+    const int32_t u = __builtin_amdgcn_readfirstlane(meta[2 * i + 1]);
     const int32_t col = u * kUnit + 4 * lane;
 #pragma unroll
     for (int j = 0; j < NN; ++j) {
@@ -474,10 +491,11 @@ __device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* st
 }
 
 template <class Fmt, int NN>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBlockThreads)
+__attribute__((amdgpu_waves_per_eu(Fmt::waves_per_simd(NN), Fmt::waves_per_simd(NN))))
 void logits_kernel(const LogitsArgs a) {
-  __shared__ float stage_all[kWavesPerBlock][Stage<NN>::kFloats];
-  __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<NN>::kUnits];
+  __shared__ float stage_all[kWavesPerBlock][Stage<Fmt, NN>::kFloats];
+  __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<Fmt, NN>::kUnits];
   __shared__ __attribute__((aligned(16))) uint8_t xpose_all[kWavesPerBlock][Fmt::kLdsBytes > 0 ? Fmt::kLdsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -499,11 +517,14 @@ void logits_kernel(const LogitsArgs a) {
   // K ring: page p of a unit always lives in slot p, so the 4 pages of the
   // next unit are in flight while the current one is consumed.
   typename Fmt::KFrag ring[kPagesPerUnit];
-  RowState<Fmt, NN> rs;
-  rs.b = -1;
 #pragma unroll
   for (int p = 0; p < kPagesPerUnit; ++p) load_page<Fmt>(a, cur, p, rows, lane, ring[p]);
+  RowState<Fmt, NN> rs;
+  rs.b = -1;
   int32_t staged = 0;
+  // One exit, after the flush of the last unit, so the load counter has the
+  // same history on every path into the loop head and each page waits only
+  // for its own loads.
   while (true) {
     if (cur.b != rs.b) {  // new batch row: its query block and weights
       load_row<Fmt, NN>(a, cur.b, lane, rs);
@@ -525,7 +546,7 @@ void logits_kernel(const LogitsArgs a) {
     }
     ++staged;
     const bool last = !it.valid(nxt);
-    if (staged == Stage<NN>::kUnits || last) {
+    if (staged == Stage<Fmt, NN>::kUnits || last) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       flush_stage<NN>(a, stage, meta, staged, lane);
