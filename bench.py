@@ -36,14 +36,16 @@ METRIC = "KV tokens scored/s + achieved HBM GB/s, fp8 paged MQA logits, B=2048 d
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "large_fp8"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_fp8_large_fp8_traffic.txt")
-KERNEL_SOURCES = ["logits_kernel.hpp", "logits_fp8.hip", "tail_fill.hip", "pmqa_internal.h",
-                  "api.cpp"]
+# Sources (under paged_mqa_logits_amd/) that determine the timed kernels,
+# compile flags included.
+KERNEL_SOURCES = ["csrc/logits_kernel.hpp", "csrc/logits_fp8.hip", "csrc/tail_fill.hip",
+                  "csrc/pmqa_internal.h", "csrc/api.cpp", "build.py"]
 
 
 def kernel_source_hash():
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_mqa_logits_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "paged_mqa_logits_amd", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -219,15 +221,30 @@ def main():
     torch.cuda.synchronize()
     k_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)])
     k_mean = float(k_ms.mean())
-    # schedule kernel alone
-    es0 = torch.cuda.Event(enable_timing=True)
-    es1 = torch.cuda.Event(enable_timing=True)
-    es0.record(stream)
-    for _ in range(args.steps):
-        pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
-    es1.record(stream)
-    torch.cuda.synchronize()
-    s_mean = es0.elapsed_time(es1) / args.steps
+    # schedule calls alone, back to back on the stream (us per call): the
+    # binary search, the linear scan it replaced, and refresh_schedule keeping
+    # a fresh schedule or rebuilding a stale one (header word cleared first)
+    def per_call_us(fn, n=max(args.steps, 20)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    spare = torch.empty_like(sched)
+    ctx_dev = dev["context_lens"]
+    poke = lambda: spare[:1].fill_(0)
+    sched_us = {
+        "binary": per_call_us(lambda: pmqa.compute_schedule(ctx_dev, num_workers=W, out=spare)),
+        "linear": per_call_us(lambda: pmqa.compute_schedule_linear(ctx_dev, num_workers=W,
+                                                                   out=spare)),
+        "refresh_keep": per_call_us(lambda: pmqa.refresh_schedule(ctx_dev, spare, num_workers=W)),
+    }
+    sched_us["refresh_rebuild"] = per_call_us(
+        lambda: (poke(), pmqa.refresh_schedule(ctx_dev, spare, num_workers=W))) - per_call_us(poke)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
@@ -288,7 +305,7 @@ def main():
         "algorithmic_bytes_per_step": alg,
         "logits_call_us": {"mean": k_mean * 1e3, "p10": float(np.percentile(k_ms, 10)) * 1e3,
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
-        "schedule_kernel_us": s_mean * 1e3,
+        "schedule_us": {k: round(v, 2) for k, v in sched_us.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "

@@ -117,6 +117,49 @@ pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32
                                int32_t* schedule, hipStream_t stream);
 
 /*
+ * compute_schedule_linear - the same schedule, each worker's start found by
+ * a linear scan of the prefix sums.
+ *
+ * Page: section 1, third bullet: the partition search before the change was
+ * a linear scan, and at batch 2048 the binary search cut the runtime launch
+ * cost tenfold.  The result is identical to compute_schedule's word for
+ * word; this entry point exists to measure that cost on the same device.
+ * Arguments, buffer layout, errors and graph capture as compute_schedule.
+ */
+pmqa_status_t compute_schedule_linear(const int32_t* context_lens, int32_t batch,
+                                      int32_t num_workers, int32_t* schedule,
+                                      hipStream_t stream);
+
+/*
+ * refresh_schedule - reuse a schedule while it is still valid, rebuild it
+ * on the device when it is not.
+ *
+ * Page: general lessons, first item (schedule metadata may be reused, but
+ * must be recomputed whenever some ceil(context_len/256) changes) and the
+ * reviewer feedback (stale metadata under graph reuse; recompute when a
+ * length crosses a 256-token boundary).
+ *
+ *   context_lens, batch, num_workers   as compute_schedule.
+ *   schedule      int32 buffer of pmqa_schedule_bytes(batch, num_workers)
+ *                 bytes: read, and rewritten only when stale.  It is kept
+ *                 as is when its header holds the magic, this batch and
+ *                 num_workers, unit 256 and T = S[batch], S[0] = 0, and
+ *                 S[b+1] - S[b] = ceil(context_lens[b]/256) for every row;
+ *                 otherwise it is rebuilt with exactly the contents
+ *                 compute_schedule writes.  The worker starts are not
+ *                 re-checked: a buffer last written by compute_schedule (or
+ *                 by this call) for the same batch and num_workers is valid
+ *                 whenever those checks pass.
+ *   recomputed    NULL, or a device int32 that receives 1 when the buffer
+ *                 was rebuilt and 0 when it was kept (4-byte aligned).
+ *
+ * One workgroup; no host synchronization; can be captured into a graph and
+ * replayed as lengths grow.  Errors as compute_schedule.
+ */
+pmqa_status_t refresh_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                               int32_t* schedule, int32_t* recomputed, hipStream_t stream);
+
+/*
  * paged_mqa_logits_fp8 - logits from an fp8 paged K cache.
  *
  * Page: introduction (fp8 kernel, weighted sum of rectified scores) and

@@ -4,11 +4,13 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/pmqa.h``.  torch provides
 device memory and the current stream; tensors are passed as raw pointers.
 There is no fallback: importing this package fails if the library has not
-been built (``python -m paged_mqa_logits_amd.build``).
+been built (``python paged_mqa_logits_amd/build.py``).
 
 Entry points (same names as the C ABI):
 
     compute_schedule(context_lens, num_workers=None, out=None) -> schedule
+    compute_schedule_linear(context_lens, num_workers=None, out=None) -> schedule
+    refresh_schedule(context_lens, schedule, num_workers=None, recomputed=None)
     paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table,
                          schedule, max_context_len, out=None) -> logits
     paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
@@ -41,7 +43,8 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED
           5: "PMQA_ERR_CAPTURING", 6: "PMQA_ERR_HIP"}
 
 EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
-           "compute_schedule", "paged_mqa_logits_fp8", "paged_mqa_logits_fp4")
+           "compute_schedule", "compute_schedule_linear", "refresh_schedule",
+           "paged_mqa_logits_fp8", "paged_mqa_logits_fp4")
 
 
 class PmqaError(RuntimeError):
@@ -55,7 +58,7 @@ class PmqaError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m paged_mqa_logits_amd.build` (hipcc, gfx950)")
+                      "`python paged_mqa_logits_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -68,6 +71,10 @@ _lib.pmqa_default_num_workers.restype = ctypes.c_int
 _lib.pmqa_default_num_workers.argtypes = [ctypes.c_int, _i32, _i32, ctypes.POINTER(_i32)]
 _lib.compute_schedule.restype = ctypes.c_int
 _lib.compute_schedule.argtypes = [_p, _i32, _i32, _p, _p]
+_lib.compute_schedule_linear.restype = ctypes.c_int
+_lib.compute_schedule_linear.argtypes = [_p, _i32, _i32, _p, _p]
+_lib.refresh_schedule.restype = ctypes.c_int
+_lib.refresh_schedule.argtypes = [_p, _i32, _i32, _p, _p, _p]
 _lib.paged_mqa_logits_fp8.restype = ctypes.c_int
 _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                       _i64, _i32, _i32, _i64, _i32, _p]
@@ -126,9 +133,7 @@ def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None):
     return int(out.value)
 
 
-def compute_schedule(context_lens, num_workers=None, out=None, variant=VARIANT_FP8, next_n=1,
-                     stream=None):
-    """Schedule (int32 tensor) of the persistent workers for these lengths."""
+def _schedule_buffer(context_lens, num_workers, out, variant, next_n):
     _need(context_lens, "context_lens", (torch.int32,), ndim=1)
     B = context_lens.shape[0]
     W = default_num_workers(variant, next_n) if num_workers is None else int(num_workers)
@@ -139,8 +144,37 @@ def compute_schedule(context_lens, num_workers=None, out=None, variant=VARIANT_F
         _need(out, "out", (torch.int32,))
         if out.numel() < words:
             raise ValueError(f"schedule buffer has {out.numel()} words, needs {words}")
+    return B, W, out
+
+
+def compute_schedule(context_lens, num_workers=None, out=None, variant=VARIANT_FP8, next_n=1,
+                     stream=None):
+    """Schedule (int32 tensor) of the persistent workers for these lengths."""
+    B, W, out = _schedule_buffer(context_lens, num_workers, out, variant, next_n)
     _check(_lib.compute_schedule(_ptr(context_lens), B, W, _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def compute_schedule_linear(context_lens, num_workers=None, out=None, variant=VARIANT_FP8,
+                            next_n=1, stream=None):
+    """The same schedule, worker starts found by a linear scan (for timing)."""
+    B, W, out = _schedule_buffer(context_lens, num_workers, out, variant, next_n)
+    _check(_lib.compute_schedule_linear(_ptr(context_lens), B, W, _ptr(out),
+                                        _stream_ptr(stream)))
+    return out
+
+
+def refresh_schedule(context_lens, schedule, num_workers=None, recomputed=None,
+                     variant=VARIANT_FP8, next_n=1, stream=None):
+    """Rebuild `schedule` in place on the device only if it no longer matches
+    these lengths; `recomputed` (optional int32 device tensor, 1 element)
+    receives 1 after a rebuild, 0 otherwise.  Returns `schedule`."""
+    B, W, schedule = _schedule_buffer(context_lens, num_workers, schedule, variant, next_n)
+    if recomputed is not None:
+        _need(recomputed, "recomputed", (torch.int32,))
+    _check(_lib.refresh_schedule(_ptr(context_lens), B, W, _ptr(schedule), _ptr(recomputed),
+                                 _stream_ptr(stream)))
+    return schedule
 
 
 def schedule_workers(schedule):

@@ -1,6 +1,7 @@
 """Build the HIP library ``libpmqa.so`` in-tree for gfx950.
 
-Usage: ``python -m paged_mqa_logits_amd.build`` (or ``build()`` from Python).
+Usage: ``python paged_mqa_logits_amd/build.py`` (run as a script: importing the
+package would first load the library this builds).
 Every HIP translation unit is compiled with hipcc for gfx950 only, with packed
 fp32 instructions disabled, then linked into one shared library next to this
 file, where the Python binding loads it.

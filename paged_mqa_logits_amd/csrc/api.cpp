@@ -254,8 +254,10 @@ pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next
   return ok();
 }
 
-pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
-                               int32_t* schedule, hipStream_t stream) {
+namespace {
+
+pmqa_status_t check_schedule_args(const int32_t* context_lens, int32_t batch,
+                                  int32_t num_workers, const int32_t* schedule) {
   if (!context_lens) return fail(PMQA_ERR_INVALID_ARGUMENT, "context_lens is null");
   if (!schedule) return fail(PMQA_ERR_INVALID_ARGUMENT, "schedule is null");
   if (!aligned(context_lens, 4) || !aligned(schedule, 4))
@@ -265,10 +267,41 @@ pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32
     return fail(PMQA_ERR_INVALID_ARGUMENT, "num_workers = %d must be >= 1", num_workers);
   if (sched_words(batch, num_workers) > INT32_MAX)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "batch + 2*num_workers too large");
-  pmqa_status_t st = check_device(nullptr);
+  return check_device(nullptr);
+}
+
+pmqa_status_t schedule_common(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                              int32_t* schedule, bool linear, hipStream_t stream) {
+  const pmqa_status_t st = check_schedule_args(context_lens, batch, num_workers, schedule);
   if (st != PMQA_OK) return st;
-  const hipError_t e = pmqa::launch_schedule(context_lens, batch, num_workers, schedule, stream);
+  const hipError_t e =
+      pmqa::launch_schedule(context_lens, batch, num_workers, schedule, linear, stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "schedule launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                               int32_t* schedule, hipStream_t stream) {
+  return schedule_common(context_lens, batch, num_workers, schedule, false, stream);
+}
+
+pmqa_status_t compute_schedule_linear(const int32_t* context_lens, int32_t batch,
+                                      int32_t num_workers, int32_t* schedule,
+                                      hipStream_t stream) {
+  return schedule_common(context_lens, batch, num_workers, schedule, true, stream);
+}
+
+pmqa_status_t refresh_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
+                               int32_t* schedule, int32_t* recomputed, hipStream_t stream) {
+  if (recomputed && !aligned(recomputed, 4))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "recomputed must be 4-byte aligned");
+  const pmqa_status_t st = check_schedule_args(context_lens, batch, num_workers, schedule);
+  if (st != PMQA_OK) return st;
+  const hipError_t e = pmqa::launch_refresh_schedule(context_lens, batch, num_workers, schedule,
+                                                     recomputed, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "refresh launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -78,8 +78,10 @@ __device__ __forceinline__ int32_t sload(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane(*(cint_ptr)(p));
 }
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+// bytes is the unsigned 32-bit record count (up to 2^32 - 1).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int32_t)bytes,
+                                           kRsrcWord3);
 }
 
 // Read-only view of a schedule; every index derived from it is clamped.
@@ -478,13 +480,15 @@ __device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* st
     for (int j = 0; j < NN; ++j) {
       const int64_t r = (int64_t)b * NN + j;
       const v4f v = *reinterpret_cast<const v4f*>(stage + (i * NN + j) * kUnit + 4 * lane);
-      const rsrc_t orow = make_rsrc(a.out + r * a.ldo, a.max_ctx * 4);
+      const rsrc_t orow = make_rsrc(a.out + r * a.ldo, 4u * (uint32_t)a.max_ctx);
       if (u * kUnit + kUnit <= a.max_ctx) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), orow, 4 * col, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), orow,
+                                               (int32_t)(4u * (uint32_t)col), 0, 0);
       } else {  // unit crosses max_ctx: per-column stores, the rest is dropped
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[e]), orow, 4 * (col + e), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[e]), orow,
+                                                (int32_t)(4u * (uint32_t)(col + e)), 0, 0);
       }
     }
   }

@@ -39,8 +39,13 @@ struct LogitsArgs {
 };
 
 // Launchers (defined next to their kernels).  Return the launch status.
+// linear: find worker starts by a linear scan instead of a binary search
+// (same result).
 hipError_t launch_schedule(const int32_t* ctx, int32_t batch, int32_t num_workers,
-                           int32_t* sched, hipStream_t stream);
+                           int32_t* sched, bool linear, hipStream_t stream);
+// Rebuilds sched only when it does not match (batch, num_workers, ctx).
+hipError_t launch_refresh_schedule(const int32_t* ctx, int32_t batch, int32_t num_workers,
+                                   int32_t* sched, int32_t* recomputed, hipStream_t stream);
 hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, hipStream_t stream);
 hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream);
 // -inf over columns [0, max_ctx) of every output row (runs before the unit

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pmqa.h")
 
 pmqa = pytest.importorskip("paged_mqa_logits_amd",
-                           reason="libpmqa.so not built (python -m paged_mqa_logits_amd.build)")
+                           reason="libpmqa.so not built (python paged_mqa_logits_amd/build.py)")
 
 
 def _declared_functions():
@@ -101,12 +101,22 @@ def test_fp4_null_q_scale():
     ((FAKE, 4, 0, FAKE), "num_workers"),
     ((FAKE + 1, 4, 8, FAKE), "aligned"),
 ])
-def test_schedule_argument_checks(args, needle):
+@pytest.mark.parametrize("entry", ["compute_schedule", "compute_schedule_linear",
+                                   "refresh_schedule"])
+def test_schedule_argument_checks(args, needle, entry):
     lib = pmqa.library()
     p = ctypes.c_void_p
     ctx, B, W, out = args
-    st = lib.compute_schedule(p(ctx), B, W, p(out), p(0))
+    extra = (p(0),) if entry == "refresh_schedule" else ()
+    st = getattr(lib, entry)(p(ctx), B, W, p(out), *extra, p(0))
     assert st == 1 and needle in pmqa.last_error()
+
+
+def test_refresh_schedule_flag_alignment():
+    lib = pmqa.library()
+    p = ctypes.c_void_p
+    st = lib.refresh_schedule(p(FAKE), 4, 8, p(FAKE), p(FAKE + 2), p(0))
+    assert st == 1 and "recomputed" in pmqa.last_error()
 
 
 def test_default_num_workers_argument_checks():

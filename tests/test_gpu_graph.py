@@ -13,12 +13,14 @@ pytestmark = pytest.mark.gpu
 pmqa = pytest.importorskip("paged_mqa_logits_amd")
 
 
-def test_graph_replay_tracks_context_lengths():
+@pytest.mark.parametrize("mode", ["compute", "refresh"])
+def test_graph_replay_tracks_context_lengths(mode):
     """Capture schedule + logits once; each step updates context_lens in place
     (some rows cross a 256-token boundary) and replays.  Every replay must
     match the oracle for that step's lengths.  Eager work and synchronizations
-    sit between replays."""
-    announce("graph replay")
+    sit between replays.  In refresh mode the schedule is rebuilt on the
+    device only on the steps where some row's unit count changed."""
+    announce(f"graph replay ({mode})")
     B, M = 24, 2048
     rng = np.random.default_rng(80)
     ctx0 = rng.integers(0, 1700, size=B).astype(np.int32)
@@ -32,8 +34,13 @@ def test_graph_replay_tracks_context_lengths():
     sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
     out = torch.empty((B, M), dtype=torch.float32, device="cuda")
 
+    flag = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+
     def step():
-        pmqa.compute_schedule(ctx_t, num_workers=W, out=sched)
+        if mode == "compute":
+            pmqa.compute_schedule(ctx_t, num_workers=W, out=sched)
+        else:
+            pmqa.refresh_schedule(ctx_t, sched, num_workers=W, recomputed=flag)
         pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], ctx_t,
                                   dev["block_table"], sched, M, out=out, num_workers=W)
 
@@ -49,7 +56,9 @@ def test_graph_replay_tracks_context_lengths():
     torch.cuda.synchronize()
 
     ctx = ctx0.copy()
+    rebuilt = 0
     for it in range(6):
+        prev = ctx.copy()
         if it:
             grow = np.where(ctx > 0, 1 + 37 * (it % 2), 0).astype(np.int32)
             ctx = ctx + grow
@@ -60,6 +69,11 @@ def test_graph_replay_tracks_context_lengths():
         got = out.cpu().numpy()
         ref = oracle(dict(d, context_lens=ctx))
         parity.check(got, ref, f"replay {it}")
+        if mode == "refresh":
+            crossed = bool(np.any((ctx + 255) // 256 != (prev + 255) // 256))
+            assert int(flag.item()) == int(crossed), it
+            rebuilt += crossed
+    assert mode == "compute" or 0 < rebuilt < 6
 
 
 def test_validate_mode_detects_stale_schedule(monkeypatch):

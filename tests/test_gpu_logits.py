@@ -108,6 +108,37 @@ def test_fp4_small_full():
     parity.check(lg, oracle(d), "fp4 small")
 
 
+def test_tail_columns_covered():
+    """Every column is written, by the -inf fill or by a unit: truncated rows
+    (context past max_context_len), a width that is not a multiple of 4 or
+    256, two query rows per batch row, several worker counts, on a poisoned
+    output."""
+    announce("tail coverage")
+    rng = np.random.default_rng(74)
+    M = 1001
+    ctx = rng.integers(0, 1600, size=300)
+    ctx[rng.random(300) < 0.2] = 0
+    ctx[::17] = M + 300
+    d = make_fp8(ctx, next_n=2, max_context_len=M, seed=74, bt_stride=-(-1900 // 64))
+    ref = oracle(d)
+    dev = upload(d)
+    for W in (1, 7, 1024):
+        lg, _ = run(d, dev=dev, num_workers=W)
+        parity.check(lg, ref, f"tail coverage W={W}")
+
+
+def test_large_batch_of_short_rows():
+    """16385 batch rows, most of them empty: the schedule's prefix sums no
+    longer fit its LDS table and are searched in global memory."""
+    announce("batch 16385 short rows")
+    rng = np.random.default_rng(75)
+    ctx = rng.integers(1, 300, size=16385)
+    ctx[rng.random(16385) < 0.9] = 0
+    d = make_fp8(ctx, next_n=1, max_context_len=299, seed=75)
+    lg, _ = run(d)
+    parity.check(lg, oracle(d), "batch 16385")
+
+
 # ---------------------------------------------------------------- self-consistency
 
 def test_worker_count_invariance_and_determinism():
