@@ -119,6 +119,39 @@ def cpu_baseline(data, n_rows, seed):
             "sample": f"{len(rows)} of {B} rows (seeded), {toks} KV tokens, {dt:.1f} s"}
 
 
+def measure_append(pmqa, torch, batch, reps=20):
+    """quantize_append_fp8/fp4 with bf16 input: one token per batch row (a
+    decode step) and 2^20 tokens into whole pages placed at random (a
+    prefill).  Algorithmic bytes per token: 256 in + 8 slot + the page bytes
+    of one token (132 fp8, 68 fp4)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for variant, page_bytes, fn in (("fp8", pmqa.FP8_PAGE_BYTES, pmqa.quantize_append_fp8),
+                                    ("fp4", pmqa.FP4_PAGE_BYTES, pmqa.quantize_append_fp4)):
+        for label, n in (("decode", batch), ("prefill", 1 << 20)):
+            pages = (n + 63) // 64
+            cache = torch.zeros((pages, page_bytes), dtype=torch.uint8, device="cuda")
+            k = torch.randn((n, 128), generator=gen, device="cuda").to(torch.bfloat16)
+            perm = torch.randperm(pages, generator=gen, device="cuda")
+            idx = torch.arange(n, device="cuda")
+            slots = perm[idx // 64] * 64 + idx % 64
+            fn(k, slots, cache)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn(k, slots, cache)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            alg = n * (256 + 8 + page_bytes // 64)
+            out[f"{variant}_{label}"] = {"tokens": n, "us": round(us, 2),
+                                         "gbps": round(alg / (us * 1e-6) / 1e9, 1)}
+            del cache, k, perm, idx, slots
+    return out
+
+
 def describe(cfg):
     if cfg.ctx_kind == "lognormal":
         dist = (f"ctx lognormal(median {cfg.ctx_median:g}, sigma {cfg.ctx_sigma:g}) clipped "
@@ -246,6 +279,8 @@ def main():
     sched_us["refresh_rebuild"] = per_call_us(
         lambda: (poke(), pmqa.refresh_schedule(ctx_dev, spare, num_workers=W))) - per_call_us(poke)
 
+    append = measure_append(pmqa, torch, B)
+
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -306,6 +341,7 @@ def main():
         "logits_call_us": {"mean": k_mean * 1e3, "p10": float(np.percentile(k_ms, 10)) * 1e3,
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
         "schedule_us": {k: round(v, 2) for k, v in sched_us.items()},
+        "append": append,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "

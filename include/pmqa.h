@@ -72,6 +72,9 @@ typedef enum {
 
 typedef enum { PMQA_VARIANT_FP8 = 0, PMQA_VARIANT_FP4 = 1 } pmqa_variant_t;
 
+/* Element type of the K values given to the quantize_append calls. */
+typedef enum { PMQA_DTYPE_F32 = 0, PMQA_DTYPE_BF16 = 1 } pmqa_dtype_t;
+
 /* Message of the last failing call on this thread ("" after success).  The
  * string is owned by the library and valid until the next call on the
  * thread. */
@@ -216,6 +219,50 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
                                    int64_t num_pages, int32_t block_table_stride,
                                    int32_t max_context_len, int64_t logits_stride,
                                    int32_t num_workers, hipStream_t stream);
+
+/*
+ * quantize_append_fp8 / quantize_append_fp4 - quantize new K tokens and
+ * write them into the paged cache the logits calls read.
+ *
+ * Page: introduction (the fp8 and fp4 paged K caches the two kernels
+ * consume).  The page does not say how the cache is written; these calls
+ * use the plainest rules of the two formats:
+ *   fp8:   per token, scale = amax/448 (fp32, nearest even) stored as the
+ *          token's fp32 scale; each value becomes the E4M3fn byte nearest
+ *          to x/scale (|x/scale| clamped to 448), ties to the even code,
+ *          sign bit = sign of x/scale; an all-zero token gets scale 0 and
+ *          zero bytes.
+ *   MXFP4: per 32 values, e = floor(log2 amax) - 2 clamped to [-127, 127],
+ *          stored as the E8M0 byte e+127 (0 for an all-zero block); each
+ *          value becomes the E2M1 code nearest to |x|*2^-e, ties to the even
+ *          code, saturating at 6, sign bit only on a non-zero magnitude;
+ *          value 2i is the low nibble of byte i.
+ *
+ *   k             [num_tokens, head_dim] row-major values of type k_dtype
+ *                 (PMQA_DTYPE_F32 or PMQA_DTYPE_BF16), 16-byte aligned,
+ *                 finite.
+ *   num_tokens    >= 0 (0: nothing is read or written).
+ *   head_dim      must be 128.
+ *   slot_mapping  int64 [num_tokens], 8-byte aligned: token i goes to page
+ *                 slot/64, row slot%64.  A negative slot skips the token;
+ *                 a slot at or past num_pages*64 is skipped too (validate
+ *                 mode reports it as PMQA_ERR_INVALID_VALUE).  Slots must be
+ *                 distinct (validate mode checks); two tokens with one slot
+ *                 leave that row unspecified.
+ *   kv_cache      [num_pages][PMQA_FP8_PAGE_BYTES] (fp8) or
+ *                 [num_pages][PMQA_FP4_PAGE_BYTES] (fp4) bytes, 16-byte
+ *                 aligned; only the rows and scales of the given slots are
+ *                 written.
+ *
+ * One wavefront per token; no host synchronization outside validate mode;
+ * can be captured into a graph.
+ */
+pmqa_status_t quantize_append_fp8(const void* k, int32_t k_dtype, int64_t num_tokens,
+                                  int32_t head_dim, const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_pages, hipStream_t stream);
+pmqa_status_t quantize_append_fp4(const void* k, int32_t k_dtype, int64_t num_tokens,
+                                  int32_t head_dim, const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_pages, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
                          schedule, max_context_len, out=None) -> logits
     paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
                          block_table, schedule, max_context_len, out=None)
+    quantize_append_fp8(k, slot_mapping, kv_cache) -> kv_cache
+    quantize_append_fp4(k, slot_mapping, kv_cache) -> kv_cache
     default_num_workers(variant, next_n=1, device=None)
     schedule_bytes(batch, num_workers)
 """
@@ -44,7 +46,8 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED
 
 EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
            "compute_schedule", "compute_schedule_linear", "refresh_schedule",
-           "paged_mqa_logits_fp8", "paged_mqa_logits_fp4")
+           "paged_mqa_logits_fp8", "paged_mqa_logits_fp4", "quantize_append_fp8",
+           "quantize_append_fp4")
 
 
 class PmqaError(RuntimeError):
@@ -78,6 +81,10 @@ _lib.refresh_schedule.argtypes = [_p, _i32, _i32, _p, _p, _p]
 _lib.paged_mqa_logits_fp8.restype = ctypes.c_int
 _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                       _i64, _i32, _i32, _i64, _i32, _p]
+_lib.quantize_append_fp8.restype = ctypes.c_int
+_lib.quantize_append_fp8.argtypes = [_p, _i32, _i64, _i32, _p, _p, _i64, _p]
+_lib.quantize_append_fp4.restype = ctypes.c_int
+_lib.quantize_append_fp4.argtypes = [_p, _i32, _i64, _i32, _p, _p, _i64, _p]
 _lib.paged_mqa_logits_fp4.restype = ctypes.c_int
 _lib.paged_mqa_logits_fp4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                       _i32, _i64, _i32, _i32, _i64, _i32, _p]
@@ -257,3 +264,33 @@ def _sched_workers(schedule, batch, num_workers):
         raise ValueError(f"schedule of {words} words does not fit batch {batch}; "
                          "pass num_workers explicitly")
     return w2 // 2
+
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def _append(fn, k, slot_mapping, kv_cache, page_bytes, stream):
+    _need(k, "k", (torch.float32, torch.bfloat16), ndim=2)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), ndim=1)
+    _need(kv_cache, "kv_cache", _BYTE, ndim=2)
+    if kv_cache.shape[1] != page_bytes:
+        raise ValueError(f"kv_cache rows must be {page_bytes} bytes, got {kv_cache.shape[1]}")
+    if slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping must have one entry per token of k")
+    dtype = DTYPE_F32 if k.dtype == torch.float32 else DTYPE_BF16
+    _check(fn(_ptr(k), dtype, k.shape[0], k.shape[1], _ptr(slot_mapping), _ptr(kv_cache),
+              kv_cache.shape[0], _stream_ptr(stream)))
+    return kv_cache
+
+
+def quantize_append_fp8(k, slot_mapping, kv_cache, stream=None):
+    """Quantize K tokens [n, 128] (fp32 or bf16) to E4M3 + fp32 scale and
+    write them into the fp8 paged cache at slot_mapping (page*64 + row)."""
+    return _append(_lib.quantize_append_fp8, k, slot_mapping, kv_cache, FP8_PAGE_BYTES, stream)
+
+
+def quantize_append_fp4(k, slot_mapping, kv_cache, stream=None):
+    """Quantize K tokens [n, 128] (fp32 or bf16) to MXFP4 and write them into
+    the fp4 paged cache at slot_mapping (page*64 + row)."""
+    return _append(_lib.quantize_append_fp4, k, slot_mapping, kv_cache, FP4_PAGE_BYTES, stream)

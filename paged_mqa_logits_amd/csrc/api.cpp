@@ -13,6 +13,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -281,6 +282,86 @@ pmqa_status_t schedule_common(const int32_t* context_lens, int32_t batch, int32_
 }
 
 }  // namespace
+
+namespace {
+
+// Validate mode for the append calls: every slot below num_pages * 64 (or
+// negative), and no slot written twice.
+pmqa_status_t validate_slots(const int64_t* slots, int64_t n, int64_t num_pages,
+                             hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(PMQA_ERR_CAPTURING, "PMQA_VALIDATE_INPUTS is set but the stream is capturing");
+  std::vector<int64_t> h((size_t)n);
+  e = hipMemcpyAsync(h.data(), slots, (size_t)n * 8, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "validate copy: %s", hipGetErrorString(e));
+  for (int64_t i = 0; i < n; ++i)
+    if (h[i] >= num_pages * pmqa::kPage)
+      return fail(PMQA_ERR_INVALID_VALUE, "slot_mapping[%lld] = %lld outside [0, %lld)",
+                  (long long)i, (long long)h[i], (long long)(num_pages * pmqa::kPage));
+  std::sort(h.begin(), h.end());
+  for (size_t i = 1; i < h.size(); ++i)
+    if (h[i] >= 0 && h[i] == h[i - 1])
+      return fail(PMQA_ERR_INVALID_VALUE, "slot %lld appears twice in slot_mapping",
+                  (long long)h[i]);
+  return PMQA_OK;
+}
+
+pmqa_status_t append_common(int variant, const void* k, int32_t k_dtype, int64_t num_tokens,
+                            int32_t head_dim, const int64_t* slot_mapping, void* kv_cache,
+                            int64_t num_pages, hipStream_t stream) {
+  if (num_tokens < 0)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_tokens = %lld must be >= 0",
+                (long long)num_tokens);
+  if (num_tokens > (int64_t)INT32_MAX * 4)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_tokens = %lld too large", (long long)num_tokens);
+  if (k_dtype != pmqa::kDtypeF32 && k_dtype != pmqa::kDtypeBf16)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "k_dtype = %d is neither PMQA_DTYPE_F32 nor "
+                "PMQA_DTYPE_BF16", k_dtype);
+  if (head_dim != pmqa::kHeadDim)
+    return fail(PMQA_ERR_UNSUPPORTED, "head_dim = %d (compiled: %d)", head_dim, pmqa::kHeadDim);
+  if (num_pages < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "num_pages = %lld must be >= 1",
+                (long long)num_pages);
+  if (!kv_cache) return fail(PMQA_ERR_INVALID_ARGUMENT, "kv_cache is null");
+  if (!aligned(kv_cache, 16))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "kv_cache must be 16-byte aligned");
+  if (num_tokens == 0) return ok();  // nothing to read or write
+  if (!k) return fail(PMQA_ERR_INVALID_ARGUMENT, "k is null");
+  if (!slot_mapping) return fail(PMQA_ERR_INVALID_ARGUMENT, "slot_mapping is null");
+  if (!aligned(k, 16)) return fail(PMQA_ERR_INVALID_ARGUMENT, "k must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
+  pmqa_status_t st = check_device(nullptr);
+  if (st != PMQA_OK) return st;
+  if (validate_mode()) {
+    st = validate_slots(slot_mapping, num_tokens, num_pages, stream);
+    if (st != PMQA_OK) return st;
+  }
+  const hipError_t e = pmqa::launch_append(variant, k, k_dtype, num_tokens, slot_mapping,
+                                           static_cast<uint8_t*>(kv_cache), num_pages, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+pmqa_status_t quantize_append_fp8(const void* k, int32_t k_dtype, int64_t num_tokens,
+                                  int32_t head_dim, const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_pages, hipStream_t stream) {
+  return append_common(0, k, k_dtype, num_tokens, head_dim, slot_mapping, kv_cache, num_pages,
+                       stream);
+}
+
+pmqa_status_t quantize_append_fp4(const void* k, int32_t k_dtype, int64_t num_tokens,
+                                  int32_t head_dim, const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_pages, hipStream_t stream) {
+  return append_common(1, k, k_dtype, num_tokens, head_dim, slot_mapping, kv_cache, num_pages,
+                       stream);
+}
 
 pmqa_status_t compute_schedule(const int32_t* context_lens, int32_t batch, int32_t num_workers,
                                int32_t* schedule, hipStream_t stream) {

@@ -53,6 +53,16 @@ hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream
 hipError_t launch_neg_inf_fill(float* out, int64_t ldo, int64_t rows, int32_t max_ctx,
                                int32_t blocks, hipStream_t stream);
 
+// Element types of the K values handed to the append kernels.
+constexpr int32_t kDtypeF32 = 0;
+constexpr int32_t kDtypeBf16 = 1;
+// Quantize n tokens of K [n, 128] (fp32 or bf16) into the paged cache at
+// slots[i] = page * 64 + row; negative slots and pages >= num_pages are
+// skipped.  variant 0 = fp8 pages, 1 = MXFP4 pages.
+hipError_t launch_append(int variant, const void* k, int32_t dtype, int64_t n,
+                         const int64_t* slots, uint8_t* kv, int64_t num_pages,
+                         hipStream_t stream);
+
 // Resident workgroups per compute unit of a logits kernel (occupancy query).
 hipError_t logits_blocks_per_cu(int variant, int next_n, int* blocks);
 
