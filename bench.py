@@ -281,6 +281,32 @@ def main():
 
     append = measure_append(pmqa, torch, B)
 
+    # the indexer step: logits of the scheduled units, then the top k per row
+    # (no -inf fill), and the selection alone on this step's logits
+    K_TOP = 2048
+    ws = torch.empty_like(out)
+    tk_idx = torch.empty((B * NN, K_TOP), dtype=torch.int32, device="cuda")
+    tk_val = torch.empty((B * NN, K_TOP), dtype=torch.float32, device="cuda")
+
+    def topk_call():
+        if fp8:
+            pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                    dev["context_lens"], dev["block_table"], sched, M, K_TOP,
+                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W)
+        else:
+            pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
+                                    dev["context_lens"], dev["block_table"], sched, M, K_TOP,
+                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W)
+
+    pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
+    lengths = torch.from_numpy(np.clip(ctx_np.astype(np.int64).repeat(NN) - NN + 1 +
+                                       np.tile(np.arange(NN), B), 0, M).astype(np.int32)).cuda()
+    topk = {"k": K_TOP,
+            "fused_call_us": round(per_call_us(topk_call, args.steps), 2),
+            "select_only_us": round(per_call_us(
+                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val),
+                args.steps), 2)}
+
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -342,6 +368,7 @@ def main():
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
         "schedule_us": {k: round(v, 2) for k, v in sched_us.items()},
         "append": append,
+        "topk": topk,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "

@@ -221,6 +221,72 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
                                    int32_t num_workers, hipStream_t stream);
 
 /*
+ * select_topk - the k largest logits of each row, by column.
+ *
+ * Page: introduction (the logits feed the indexer, which selects KV tokens
+ * by them).  The page gives neither k nor an order; the rule here: row r's
+ * candidates are its first lengths[r] columns (clamped to
+ * [0, max_context_len]); the selection is the k largest candidates in the
+ * total order of fp32 values where -0 < +0, equal values ordered by column,
+ * lower first (NaN has no place in the order: rows holding NaN get an
+ * unspecified selection); the selected columns are written in ascending
+ * order, with their values.  A row with fewer than k candidates writes all
+ * of them and pads with column -1 and value -inf.
+ *
+ *   logits          fp32 [rows, logits_stride], 16-byte aligned; only the
+ *                   candidate columns are read.
+ *   logits_stride   >= max_context_len, multiple of 4.
+ *   rows            >= 1.
+ *   lengths         int32 [rows] candidate counts.
+ *   k               >= 1.
+ *   topk_indices    int32 [rows, topk_stride], 4-byte aligned; columns
+ *                   [0, k) written.
+ *   topk_values     fp32 [rows, topk_stride] or NULL.
+ *   topk_stride     >= k.
+ *
+ * One workgroup per row; no host synchronization; can be graph-captured.
+ */
+pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
+                          int32_t max_context_len, const int32_t* lengths, int32_t k,
+                          int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                          hipStream_t stream);
+
+/*
+ * paged_mqa_topk_fp8 / paged_mqa_topk_fp4 - the indexer step: logits of
+ * every scheduled unit, then the top k per output row.
+ *
+ * Same inputs, schedule and errors as paged_mqa_logits_fp8 / _fp4, with
+ * logits_workspace in place of the logits output: on return it holds the
+ * logits of every scheduled unit's columns (columns [0, 256*c_b) of the
+ * rows of batch row b, c_b its unit count in the schedule; -inf past a
+ * row's causal limit) and unspecified values elsewhere (no -inf fill is
+ * written).  Row r = b*next_n + j then selects as select_topk with
+ * lengths[r] = min(ctx_b - next_n + 1 + j, 256*c_b, max_context_len)
+ * (at least 0; 0 for every row when the schedule header does not describe
+ * the call).
+ *
+ *   k, topk_indices, topk_values, topk_stride   as select_topk, with
+ *                   batch*next_n rows.
+ */
+pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const float* weights,
+                                 const int32_t* context_lens, const int32_t* block_table,
+                                 const int32_t* schedule, float* logits_workspace, int32_t k,
+                                 int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                                 int32_t batch, int32_t next_n, int32_t num_heads,
+                                 int32_t head_dim, int32_t page_size, int64_t num_pages,
+                                 int32_t block_table_stride, int32_t max_context_len,
+                                 int64_t logits_stride, int32_t num_workers, hipStream_t stream);
+pmqa_status_t paged_mqa_topk_fp4(const void* q, const void* q_scale, const void* kv_cache,
+                                 const float* weights, const int32_t* context_lens,
+                                 const int32_t* block_table, const int32_t* schedule,
+                                 float* logits_workspace, int32_t k, int32_t* topk_indices,
+                                 float* topk_values, int64_t topk_stride, int32_t batch,
+                                 int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                 int32_t page_size, int64_t num_pages,
+                                 int32_t block_table_stride, int32_t max_context_len,
+                                 int64_t logits_stride, int32_t num_workers, hipStream_t stream);
+
+/*
  * quantize_append_fp8 / quantize_append_fp4 - quantize new K tokens and
  * write them into the paged cache the logits calls read.
  *

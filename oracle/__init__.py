@@ -20,6 +20,8 @@ formats       exact e4m3fn / e2m1 / e8m0 decoders built from the bit fields
 reference     the fp64 definition for the fp8 and MXFP4 variants
 exact         rational (fractions.Fraction) brute force for tiny inputs
 schedule_ref  the persistent-worker partition: linear scan and binary search
+quantize      the cache producer: fp8 and MXFP4 quantize-and-append
+topk          top-k token selection over rows of logits
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against something other than itself (library casts, brute force, closed

@@ -15,6 +15,10 @@ Entry points (same names as the C ABI):
                          schedule, max_context_len, out=None) -> logits
     paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
                          block_table, schedule, max_context_len, out=None)
+    select_topk(logits, lengths, k) -> (indices, values)
+    paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table,
+                       schedule, max_context_len, k) -> (indices, values)
+    paged_mqa_topk_fp4(q, q_scale, kv_cache, ..., k) -> (indices, values)
     quantize_append_fp8(k, slot_mapping, kv_cache) -> kv_cache
     quantize_append_fp4(k, slot_mapping, kv_cache) -> kv_cache
     default_num_workers(variant, next_n=1, device=None)
@@ -47,7 +51,7 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED
 EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
            "compute_schedule", "compute_schedule_linear", "refresh_schedule",
            "paged_mqa_logits_fp8", "paged_mqa_logits_fp4", "quantize_append_fp8",
-           "quantize_append_fp4")
+           "quantize_append_fp4", "select_topk", "paged_mqa_topk_fp8", "paged_mqa_topk_fp4")
 
 
 class PmqaError(RuntimeError):
@@ -81,6 +85,14 @@ _lib.refresh_schedule.argtypes = [_p, _i32, _i32, _p, _p, _p]
 _lib.paged_mqa_logits_fp8.restype = ctypes.c_int
 _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                       _i64, _i32, _i32, _i64, _i32, _p]
+_lib.select_topk.restype = ctypes.c_int
+_lib.select_topk.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p]
+_lib.paged_mqa_topk_fp8.restype = ctypes.c_int
+_lib.paged_mqa_topk_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _i32, _i32,
+                                    _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32, _p]
+_lib.paged_mqa_topk_fp4.restype = ctypes.c_int
+_lib.paged_mqa_topk_fp4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _i32,
+                                    _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32, _p]
 _lib.quantize_append_fp8.restype = ctypes.c_int
 _lib.quantize_append_fp8.argtypes = [_p, _i32, _i64, _i32, _p, _p, _i64, _p]
 _lib.quantize_append_fp4.restype = ctypes.c_int
@@ -200,9 +212,7 @@ def _logits_out(out, rows, max_context_len, device):
     return out, out.stride(0), out
 
 
-def paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table, schedule,
-                         max_context_len, out=None, num_workers=None, stream=None):
-    """fp8 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+def _fp8_shapes(q, kv_cache, weights, context_lens, block_table, schedule):
     _need(q, "q", _BYTE, ndim=4)
     _need(kv_cache, "kv_cache", _BYTE, ndim=2)
     _need(weights, "weights", (torch.float32,), ndim=2)
@@ -216,18 +226,10 @@ def paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table, schedu
         raise ValueError(f"weights must be [{B * NN}, {H}], got {tuple(weights.shape)}")
     if context_lens.shape[0] != B or block_table.shape[0] != B:
         raise ValueError("context_lens and block_table must have one row per batch row")
-    W = _sched_workers(schedule, B, num_workers)
-    view, ldo, buf = _logits_out(out, B * NN, int(max_context_len), q.device)
-    _check(_lib.paged_mqa_logits_fp8(
-        _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
-        _ptr(schedule), _ptr(buf), B, NN, H, D, PAGE_SIZE, kv_cache.shape[0],
-        block_table.shape[1], int(max_context_len), ldo, W, _stream_ptr(stream)))
-    return view
+    return B, NN, H, D
 
 
-def paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_table, schedule,
-                         max_context_len, out=None, num_workers=None, stream=None):
-    """MXFP4 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+def _fp4_shapes(q, q_scale, kv_cache, weights, context_lens, block_table, schedule):
     _need(q, "q", _BYTE, ndim=4)
     _need(q_scale, "q_scale", (torch.uint8, torch.float8_e8m0fnu), ndim=4)
     _need(kv_cache, "kv_cache", _BYTE, ndim=2)
@@ -244,14 +246,100 @@ def paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_tabl
         raise ValueError(f"weights must be [{B * NN}, {H}], got {tuple(weights.shape)}")
     if context_lens.shape[0] != B or block_table.shape[0] != B:
         raise ValueError("context_lens and block_table must have one row per batch row")
+    return B, NN, H, 2 * Dh
+
+
+def paged_mqa_logits_fp8(q, kv_cache, weights, context_lens, block_table, schedule,
+                         max_context_len, out=None, num_workers=None, stream=None):
+    """fp8 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+    B, NN, H, D = _fp8_shapes(q, kv_cache, weights, context_lens, block_table, schedule)
+    W = _sched_workers(schedule, B, num_workers)
+    view, ldo, buf = _logits_out(out, B * NN, int(max_context_len), q.device)
+    _check(_lib.paged_mqa_logits_fp8(
+        _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
+        _ptr(schedule), _ptr(buf), B, NN, H, D, PAGE_SIZE, kv_cache.shape[0],
+        block_table.shape[1], int(max_context_len), ldo, W, _stream_ptr(stream)))
+    return view
+
+
+def paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_table, schedule,
+                         max_context_len, out=None, num_workers=None, stream=None):
+    """MXFP4 paged MQA logits; returns fp32 [batch*next_n, max_context_len]."""
+    B, NN, H, D = _fp4_shapes(q, q_scale, kv_cache, weights, context_lens, block_table, schedule)
     W = _sched_workers(schedule, B, num_workers)
     view, ldo, buf = _logits_out(out, B * NN, int(max_context_len), q.device)
     _check(_lib.paged_mqa_logits_fp4(
         _ptr(q), _ptr(q_scale), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
-        _ptr(block_table), _ptr(schedule), _ptr(buf), B, NN, H, 2 * Dh, PAGE_SIZE,
+        _ptr(block_table), _ptr(schedule), _ptr(buf), B, NN, H, D, PAGE_SIZE,
         kv_cache.shape[0], block_table.shape[1], int(max_context_len), ldo, W,
         _stream_ptr(stream)))
     return view
+
+
+def _topk_out(indices, values, rows, k, want_values, device):
+    """Output buffers [rows, >= k] sharing one row stride."""
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=device)
+    _need(indices, "indices", (torch.int32,), ndim=2, contiguous=False)
+    if indices.shape[0] != rows or indices.shape[1] < k or indices.stride(1) != 1:
+        raise ValueError(f"indices must be [{rows}, >= {k}] with unit column stride")
+    if values is None and want_values:
+        values = torch.empty((rows, indices.stride(0)), dtype=torch.float32,
+                             device=device)[:, :indices.shape[1]]
+    if values is not None:
+        _need(values, "values", (torch.float32,), ndim=2, contiguous=False)
+        if tuple(values.shape) != tuple(indices.shape) or values.stride() != indices.stride():
+            raise ValueError("values must have the shape and strides of indices")
+    return indices, values, indices.stride(0)
+
+
+def select_topk(logits, lengths, k, indices=None, values=None, want_values=True, stream=None):
+    """Top k of each row's first lengths[r] columns, ascending column order;
+    returns (indices int32 [rows, k], values fp32 [rows, k] or None)."""
+    _need(logits, "logits", (torch.float32,), ndim=2, contiguous=False)
+    _need(lengths, "lengths", (torch.int32,), ndim=1)
+    rows, M = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    if lengths.shape[0] != rows:
+        raise ValueError("lengths must have one entry per row")
+    indices, values, ldk = _topk_out(indices, values, rows, int(k), want_values, logits.device)
+    _check(_lib.select_topk(_ptr(logits), logits.stride(0), rows, M, _ptr(lengths), int(k),
+                            _ptr(indices), _ptr(values), ldk, _stream_ptr(stream)))
+    return indices[:, :k], None if values is None else values[:, :k]
+
+
+def paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table, schedule,
+                       max_context_len, k, workspace=None, indices=None, values=None,
+                       want_values=True, num_workers=None, stream=None):
+    """The fp8 indexer step: logits of every scheduled unit into `workspace`
+    (no -inf fill), then the top k per output row; returns (indices, values)."""
+    B, NN, H, D = _fp8_shapes(q, kv_cache, weights, context_lens, block_table, schedule)
+    W = _sched_workers(schedule, B, num_workers)
+    _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
+    indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
+    _check(_lib.paged_mqa_topk_fp8(
+        _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
+        _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk, B, NN, H, D,
+        PAGE_SIZE, kv_cache.shape[0], block_table.shape[1], int(max_context_len), ldo, W,
+        _stream_ptr(stream)))
+    return indices[:, :k], None if values is None else values[:, :k]
+
+
+def paged_mqa_topk_fp4(q, q_scale, kv_cache, weights, context_lens, block_table, schedule,
+                       max_context_len, k, workspace=None, indices=None, values=None,
+                       want_values=True, num_workers=None, stream=None):
+    """The MXFP4 indexer step (see paged_mqa_topk_fp8)."""
+    B, NN, H, D = _fp4_shapes(q, q_scale, kv_cache, weights, context_lens, block_table, schedule)
+    W = _sched_workers(schedule, B, num_workers)
+    _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
+    indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
+    _check(_lib.paged_mqa_topk_fp4(
+        _ptr(q), _ptr(q_scale), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
+        _ptr(block_table), _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk,
+        B, NN, H, D, PAGE_SIZE, kv_cache.shape[0], block_table.shape[1],
+        int(max_context_len), ldo, W, _stream_ptr(stream)))
+    return indices[:, :k], None if values is None else values[:, :k]
 
 
 def _sched_workers(schedule, batch, num_workers):

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libpmqa.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "schedule.hip", "logits_fp8.hip", "logits_fp4.hip", "tail_fill.hip",
-           "append.hip"]
+           "append.hip", "topk.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]

@@ -160,11 +160,13 @@ pmqa_status_t validate_contents(const int32_t* ctx, const int32_t* bt, const int
   return PMQA_OK;
 }
 
+// fill: -inf over the columns no unit writes (the logits calls); the top-k
+// calls skip it, their selection reads only the columns the units write.
 pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, const void* kv,
                             const float* weights, const int32_t* ctx, const int32_t* bt,
                             const int32_t* sched, float* logits, const Shape& s,
                             int32_t num_heads, int32_t head_dim, int32_t page_size,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool fill = true) {
   if (!q) return fail(PMQA_ERR_INVALID_ARGUMENT, "q is null");
   if (variant == PMQA_VARIANT_FP4 && !q_scale)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "q_scale is null");
@@ -207,9 +209,12 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
   a.bt_stride = s.bt_stride;
   a.max_ctx = s.max_ctx;
   a.num_workers = s.workers;
-  hipError_t e = pmqa::launch_neg_inf_fill(logits, s.ldo, (int64_t)s.batch * s.next_n, s.max_ctx,
-                                           g_cus[dev].load(std::memory_order_acquire), stream);
-  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "-inf fill launch: %s", hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  if (fill) {
+    e = pmqa::launch_neg_inf_fill(logits, s.ldo, (int64_t)s.batch * s.next_n, s.max_ctx,
+                                  g_cus[dev].load(std::memory_order_acquire), stream);
+    if (e != hipSuccess) return fail(PMQA_ERR_HIP, "-inf fill launch: %s", hipGetErrorString(e));
+  }
   e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
                                   : pmqa::launch_logits_fp4(a, s.next_n, stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
@@ -412,6 +417,96 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
                 logits_stride};
   return logits_common(PMQA_VARIANT_FP4, q, q_scale, kv_cache, weights, context_lens,
                        block_table, schedule, logits, s, num_heads, head_dim, page_size, stream);
+}
+
+namespace {
+
+pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, int64_t ldk) {
+  if (k < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "k = %d must be >= 1", k);
+  if (!idx) return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_indices is null");
+  if (!aligned(idx, 4) || (val && !aligned(val, 4)))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_indices and topk_values must be 4-byte aligned");
+  if (ldk < k)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_stride = %lld must be >= k = %d",
+                (long long)ldk, k);
+  return PMQA_OK;
+}
+
+pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const void* kv,
+                          const float* weights, const int32_t* ctx, const int32_t* bt,
+                          const int32_t* sched, float* workspace, int32_t k, int32_t* idx,
+                          float* val, int64_t ldk, const Shape& s, int32_t num_heads,
+                          int32_t head_dim, int32_t page_size, hipStream_t stream) {
+  pmqa_status_t st = check_topk_out(k, idx, val, ldk);
+  if (st != PMQA_OK) return st;
+  st = logits_common(variant, q, q_scale, kv, weights, ctx, bt, sched, workspace, s, num_heads,
+                     head_dim, page_size, stream, /*fill=*/false);
+  if (st != PMQA_OK) return st;
+  const hipError_t e = pmqa::launch_select_topk(workspace, s.ldo, s.batch * s.next_n, s.max_ctx,
+                                                nullptr, ctx, sched, s.batch, s.next_n,
+                                                s.workers, k, idx, val, ldk, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
+                          int32_t max_context_len, const int32_t* lengths, int32_t k,
+                          int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                          hipStream_t stream) {
+  if (!logits) return fail(PMQA_ERR_INVALID_ARGUMENT, "logits is null");
+  if (!lengths) return fail(PMQA_ERR_INVALID_ARGUMENT, "lengths is null");
+  if (!aligned(logits, 16))
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "logits must be 16-byte aligned");
+  if (!aligned(lengths, 4)) return fail(PMQA_ERR_INVALID_ARGUMENT, "lengths must be 4-byte aligned");
+  if (rows < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "rows = %d must be >= 1", rows);
+  if (max_context_len < 1)
+    return fail(PMQA_ERR_INVALID_ARGUMENT, "max_context_len = %d must be >= 1", max_context_len);
+  if (logits_stride < max_context_len || logits_stride % 4 != 0)
+    return fail(PMQA_ERR_INVALID_ARGUMENT,
+                "logits_stride = %lld must be >= max_context_len and a multiple of 4",
+                (long long)logits_stride);
+  pmqa_status_t st = check_topk_out(k, topk_indices, topk_values, topk_stride);
+  if (st != PMQA_OK) return st;
+  st = check_device(nullptr);
+  if (st != PMQA_OK) return st;
+  const hipError_t e = pmqa::launch_select_topk(logits, logits_stride, rows, max_context_len,
+                                                lengths, nullptr, nullptr, 0, 1, 0, k,
+                                                topk_indices, topk_values, topk_stride, stream);
+  if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const float* weights,
+                                 const int32_t* context_lens, const int32_t* block_table,
+                                 const int32_t* schedule, float* logits_workspace, int32_t k,
+                                 int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                                 int32_t batch, int32_t next_n, int32_t num_heads,
+                                 int32_t head_dim, int32_t page_size, int64_t num_pages,
+                                 int32_t block_table_stride, int32_t max_context_len,
+                                 int64_t logits_stride, int32_t num_workers, hipStream_t stream) {
+  const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
+                logits_stride};
+  return topk_common(PMQA_VARIANT_FP8, q, nullptr, kv_cache, weights, context_lens, block_table,
+                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride, s,
+                     num_heads, head_dim, page_size, stream);
+}
+
+pmqa_status_t paged_mqa_topk_fp4(const void* q, const void* q_scale, const void* kv_cache,
+                                 const float* weights, const int32_t* context_lens,
+                                 const int32_t* block_table, const int32_t* schedule,
+                                 float* logits_workspace, int32_t k, int32_t* topk_indices,
+                                 float* topk_values, int64_t topk_stride, int32_t batch,
+                                 int32_t next_n, int32_t num_heads, int32_t head_dim,
+                                 int32_t page_size, int64_t num_pages,
+                                 int32_t block_table_stride, int32_t max_context_len,
+                                 int64_t logits_stride, int32_t num_workers, hipStream_t stream) {
+  const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
+                logits_stride};
+  return topk_common(PMQA_VARIANT_FP4, q, q_scale, kv_cache, weights, context_lens, block_table,
+                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride, s,
+                     num_heads, head_dim, page_size, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,435 @@
+// Top-k token selection over rows of logits.
+//
+// Page "[flashinfer] Blackwell 아키텍처를 위한 고성능 Paged MQA Logits 커널 도입",
+// introduction: the logits feed the indexer, which selects KV tokens by
+// them.  The page gives neither k nor an order; the rule here is: a row's
+// candidates are its first n columns, the selection is the k largest of
+// them in the total order of fp32 values with -0 < +0 (no NaN), equal values
+// ordered by column, lower first, and the selected columns are written in
+// ascending order with their values; a row with n < k writes all n and pads
+// with column -1, value -inf.
+//
+// One workgroup of 512 threads per row; wavefront w owns the contiguous
+// chunk [w*L, (w+1)*L) of the row's columns in every pass, 4 columns per
+// lane per 16-byte read.  Values are mapped to order-preserving 32-bit keys.
+//   1. One read of the row (copied into LDS when it has at most 7680
+//      columns) builds a histogram of the keys' top 11 bits; the bin that
+//      holds the k-th largest key is b.
+//   2. A second pass gathers the keys of bin b with their columns (when
+//      there are at most 1024 of them, or 3840 for a row not copied to LDS,
+//      whose gather goes where the copy would be) and counts, per wavefront,
+//      the keys
+//      above bin b.  The remaining 21 bits of the k-th largest key K are
+//      found on the gathered list alone, which also gives each wavefront's
+//      count of keys above K and equal to K.  (A larger bin is resolved with
+//      further digit passes over the row and a counting pass instead.)
+//   3. A last pass writes the selected columns in order: keys above K, and
+//      the first ones (by column) equal to K; each wavefront starts at the
+//      output position the counts give it and ranks its columns with
+//      ballots.
+// Every pass reads 8 tiles ahead (8 16-byte reads in flight per lane for a
+// row in global memory; after the first pass they hit L2).
+#include <hip/hip_runtime.h>
+
+#include "pmqa_internal.h"
+
+namespace pmqa {
+
+namespace {
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kLoads = 8;                // 16-byte reads in flight per lane
+constexpr int kTopBits = 11;             // first digit: key bits [21, 32)
+constexpr int kTopShift = 32 - kTopBits;
+constexpr int kBins = 1 << kTopBits;
+constexpr int kCand = 1024;              // gathered keys of the chosen bin of a staged row
+constexpr int kStage = 7680;             // rows up to this long are kept in LDS
+constexpr int kCandLong = kStage / 2;    // ... of a longer row (in the unused stage)
+constexpr int kBins2 = 256;              // later digits: at most 8 bits
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Larger value <-> larger key; -0 sorts just below +0.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Lanes below this one with their bit set in mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Candidates of row r: lengths[r] (clamped to [0, max_ctx]) when lengths is
+// given, else the fused indexer rule: min(causal limit, 256 c_b, max_ctx)
+// with c_b the row's unit count in the schedule (0 if the schedule header
+// does not describe this call).
+__device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
+                                                  const int32_t* lengths, const int32_t* ctx,
+                                                  const int32_t* sched, int32_t batch,
+                                                  int32_t next_n, int32_t workers) {
+  if (lengths) return min(max(lengths[r], 0), max_ctx);
+  const int32_t b = r / next_n, j = r - b * next_n;
+  const bool ok = sched[0] == kSchedMagic && sched[1] == batch && sched[2] == workers &&
+                  sched[3] >= 0;
+  const int32_t cap = (max_ctx + kUnit - 1) / kUnit;
+  int32_t c = 0;
+  if (ok) {
+    const int32_t* S = sched + kSchedHeader + 2 * (workers + 1);
+    c = min(max(S[b + 1] - S[b], 0), cap);
+  }
+  const int64_t lim = (int64_t)ctx[b] - next_n + 1 + j;
+  return (int32_t)max((int64_t)0, min(min(lim, (int64_t)kUnit * c), (int64_t)max_ctx));
+}
+
+struct SelLds {
+  union {
+    uint32_t hist[kBins];        // pass 1
+    struct {                     // after it
+      uint32_t key[kCand];
+      int32_t col[kCand];
+    } cand;
+  };
+  uint32_t hist2[kBins2];
+  union {
+    float stage[kStage] __attribute__((aligned(16)));
+    struct {
+      uint32_t key[kCandLong];
+      int32_t col[kCandLong];
+    } cand_long;
+  };
+  uint32_t wave_gt[kSelWaves], wave_eq[kSelWaves], wave_sum[kSelWaves];
+  uint32_t cand_cnt[kSelWaves];  // candidates each wavefront gathered
+  uint32_t chosen[3];  // bin, keys above it, keys in it
+  uint32_t ncand;
+};
+
+// Columns i..i+3 of a row, from LDS or global memory (two paths, so each
+// compiles to its own load instructions), columns at or past c1 as -inf.
+// Branch-free, so that several reads stay in flight: the quad read is the
+// one at i clamped to the last quad holding a column below c1 (rows are
+// allocated in whole quads: their stride is a multiple of 4), and the
+// columns past c1 are masked afterwards.
+__device__ __forceinline__ v4f load_cols(const float* row, const SelLds& lds, bool staged,
+                                         int32_t i, int32_t c1) {
+  const float ninf = -__builtin_inff();
+  const int32_t q = min(i, (c1 - 1) & ~3);
+  v4f v = staged ? *reinterpret_cast<const v4f*>(lds.stage + q)
+                 : *reinterpret_cast<const v4f*>(row + q);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = i + e < c1 ? v[e] : ninf;
+  return v;
+}
+
+// The chunk [c0, c1) a wavefront owns, read 256 columns (4 per lane) per
+// tile: calls f(first column of the lane's 4, values) for every tile in
+// column order, kLoads tiles read ahead.
+template <class F>
+__device__ __forceinline__ void for_each_tile(const float* row, const SelLds& lds, bool staged,
+                                              int32_t c0, int32_t c1, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int32_t b0 = c0; b0 < c1; b0 += kLoads * 256) {
+    v4f v[kLoads];
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m)
+      v[m] = load_cols(row, lds, staged, b0 + 256 * m + 4 * lane, c1);
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m)
+      if (b0 + 256 * m < c1) f(b0 + 256 * m + 4 * lane, v[m]);
+  }
+}
+
+// Chooses the bin of hist[0..nbins) holding the krem-th largest key (bins
+// counted from the top); every thread calls it.  Result in lds.chosen.
+__device__ __forceinline__ void choose_bin(SelLds& lds, const uint32_t* hist, int nbins,
+                                           uint32_t krem) {
+  const int per = (nbins + kSelThreads - 1) / kSelThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bhi = nbins - 1 - per * tid;
+  uint32_t own = 0;
+  for (int j = 0; j < per; ++j)
+    if (bhi - j >= 0) own += hist[bhi - j];
+  uint32_t incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) lds.wave_sum[wave] = incl;
+  __syncthreads();
+  uint32_t above = incl - own;
+  for (int w = 0; w < wave; ++w) above += lds.wave_sum[w];
+  for (int j = 0; j < per; ++j) {
+    if (bhi - j < 0) break;
+    const uint32_t h = hist[bhi - j];
+    if (above < krem && krem <= above + h) {
+      lds.chosen[0] = (uint32_t)(bhi - j);
+      lds.chosen[1] = above;
+      lds.chosen[2] = h;
+    }
+    above += h;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t max_ctx,
+                        const int32_t* __restrict__ lengths, const int32_t* __restrict__ ctx,
+                        const int32_t* __restrict__ sched, int32_t batch, int32_t next_n,
+                        int32_t workers, int32_t k, int32_t* __restrict__ out_idx,
+                        float* __restrict__ out_val, int64_t ldk) {
+  __shared__ SelLds lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t r = blockIdx.x;
+  const float* row = logits + r * ldo;
+  int32_t* oi = out_idx + r * ldk;
+  float* ov = out_val ? out_val + r * ldk : nullptr;
+  const int32_t n = row_candidates((int32_t)r, max_ctx, lengths, ctx, sched, batch, next_n,
+                                   workers);
+  const float ninf = -__builtin_inff();
+
+  if (n <= k) {  // every candidate is selected
+    for (int32_t i = tid; i < k; i += kSelThreads) {
+      oi[i] = i < n ? i : -1;
+      if (ov) ov[i] = i < n ? row[i] : ninf;
+    }
+    return;
+  }
+
+  const int32_t L = ((n + kSelWaves - 1) / kSelWaves + 3) & ~3;
+  const int32_t c0 = min(n, wave * L), c1 = min(n, c0 + L);
+  const bool staged = n <= kStage;
+
+  // 1. Histogram of the top digit (and the LDS copy of a short row).
+  for (int j = tid; j < kBins; j += kSelThreads) lds.hist[j] = 0;
+  if (tid == 0) lds.chosen[0] = lds.chosen[1] = lds.chosen[2] = 0;
+  __syncthreads();
+  for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
+    if (staged && i < c1) {
+      if (i + 4 <= c1) {
+        *reinterpret_cast<v4f*>(lds.stage + i) = v;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (i + e < c1) lds.stage[i + e] = v[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < c1) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+  });
+  __syncthreads();
+  choose_bin(lds, lds.hist, kBins, (uint32_t)k);
+  const uint32_t b1 = lds.chosen[0];
+  uint32_t krem = (uint32_t)k - lds.chosen[1];
+  const uint32_t h1 = lds.chosen[2];
+  __syncthreads();
+
+  // 2. The k-th largest key K (bits under pmask, the others free) and the
+  //    per-wavefront counts of keys above K and equal to K.
+  uint32_t pmask = ~0u << kTopShift, prefix = b1 << kTopShift;
+  bool counted = false;
+  // Wavefront w appends the keys of bin b1 it finds to its own region of
+  // the candidate buffer (R entries), so the gather needs no atomics; a
+  // region that would overflow sends the row down the slower path.
+  uint32_t* ckey = staged ? lds.cand.key : lds.cand_long.key;
+  int32_t* ccol = staged ? lds.cand.col : lds.cand_long.col;
+  const uint32_t R = (staged ? (uint32_t)kCand : (uint32_t)kCandLong) / kSelWaves;
+  if (h1 != krem && h1 <= R * kSelWaves) {
+    // gather bin b1; count the keys above it per wavefront
+    uint32_t above = 0, mine = 0;  // mine: this wavefront's candidates so far
+    for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
+      uint64_t bc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bin = order_key(v[e]) >> kTopShift;
+        const bool in = i + e < c1;
+        above += (in && bin > b1) ? 1u : 0u;
+        bc[e] = __ballot(in && bin == b1);
+      }
+      uint32_t slot = mine;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (((bc[e] >> lane) & 1u) && slot < R) {
+          ckey[wave * R + slot] = order_key(v[e]);
+          ccol[wave * R + slot] = i + e;
+        }
+        slot += (bc[e] >> lane) & 1u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
+    });
+    above = wave_sum(above);
+    if (lane == 0) {
+      lds.wave_gt[wave] = above;
+      lds.cand_cnt[wave] = mine;
+    }
+    __syncthreads();
+    bool overflow = false;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) overflow = overflow || lds.cand_cnt[w] > R;
+    if (!overflow) {
+      // resolve the low 21 bits on the gathered keys: digits of 8, 8, 5 bits
+      for (int top = kTopShift; top > 0;) {
+        const int shift = max(top - 8, 0);
+        const uint32_t dmask = (1u << (top - shift)) - 1u;
+        if (tid < kBins2) lds.hist2[tid] = 0;
+        __syncthreads();
+        for (uint32_t c = tid; c < R * kSelWaves; c += kSelThreads) {
+          const uint32_t key = ckey[c];
+          if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
+            atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        choose_bin(lds, lds.hist2, (int)dmask + 1, krem);
+        prefix |= lds.chosen[0] << shift;
+        pmask |= dmask << shift;
+        krem -= lds.chosen[1];
+        __syncthreads();
+        top = shift;
+      }
+      // each wavefront counts its own candidates above K and equal to K
+      uint32_t g = 0, q = 0;
+      for (uint32_t c = lane; c < lds.cand_cnt[wave]; c += 64) {
+        const uint32_t key = ckey[wave * R + c];
+        g += key > prefix ? 1u : 0u;
+        q += key == prefix ? 1u : 0u;
+      }
+      g = wave_sum(g);
+      q = wave_sum(q);
+      if (lane == 0) {
+        lds.wave_gt[wave] += g;
+        lds.wave_eq[wave] = q;
+      }
+      __syncthreads();
+      counted = true;
+    }
+  }
+  if (!counted && h1 != krem) {
+    // a crowded bin: further digits (8, 8, 5 bits) with passes over the row
+    for (int top = kTopShift; top > 0;) {
+      const int shift = max(top - 8, 0);
+      const uint32_t dmask = (1u << (top - shift)) - 1u;
+      if (tid < kBins2) lds.hist2[tid] = 0;
+      __syncthreads();
+      for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(v[e]);
+          if (i + e < c1 && (key & pmask) == prefix)
+            atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
+        }
+      });
+      __syncthreads();
+      choose_bin(lds, lds.hist2, (int)dmask + 1, krem);
+      prefix |= lds.chosen[0] << shift;
+      pmask |= dmask << shift;
+      const uint32_t h = lds.chosen[2];
+      krem -= lds.chosen[1];
+      __syncthreads();
+      if (h == krem) break;  // the chosen bin is taken whole
+      top = shift;
+    }
+  }
+  // Selected: keys whose bits under pmask exceed prefix, and the first krem
+  // (in column order) of those equal to it.
+  const uint32_t need_eq = krem;
+  if (!counted) {
+    uint32_t gt = 0, eq = 0;
+    for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(v[e]) & pmask;
+        const bool in = i + e < c1;
+        gt += (in && key > prefix) ? 1u : 0u;
+        eq += (in && key == prefix) ? 1u : 0u;
+      }
+    });
+    gt = wave_sum(gt);
+    eq = wave_sum(eq);
+    if (lane == 0) {
+      lds.wave_gt[wave] = gt;
+      lds.wave_eq[wave] = eq;
+    }
+    __syncthreads();
+  }
+
+  // 3. Ordered write.  Output position and equal-key rank at the start of
+  //    this wavefront's chunk:
+  uint32_t pos = 0, eq_rank = 0;
+  for (int w = 0; w < wave; ++w) {
+    const uint32_t g = lds.wave_gt[w], q = lds.wave_eq[w];
+    pos += g + (eq_rank < need_eq ? min(q, need_eq - eq_rank) : 0u);
+    eq_rank += q;
+  }
+  for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
+    if (pos >= (uint32_t)k) return;  // uniform: the wavefront's share is written
+    uint64_t bg[4], be[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = order_key(v[e]) & pmask;
+      const bool in = i + e < c1;
+      bg[e] = __ballot(in && key > prefix);
+      be[e] = __ballot(in && key == prefix);
+    }
+    // column i+e of lane l follows every column of the lanes below l and
+    // columns i..i+e-1 of lane l
+    uint32_t eq_before = 0, eq_total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      eq_before += lanes_below(be[e]);
+      eq_total += __builtin_popcountll(be[e]);
+    }
+    uint32_t my_eq = eq_rank + eq_before;
+    uint32_t sel = 0;  // bit e: column i+e selected
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool g = (bg[e] >> lane) & 1u, q = (be[e] >> lane) & 1u;
+      if (g || (q && my_eq < need_eq)) sel |= 1u << e;
+      my_eq += q ? 1u : 0u;
+    }
+    uint64_t bs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bs[e] = __ballot((sel >> e) & 1u);
+    uint32_t p = pos, total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p += lanes_below(bs[e]);
+      total += __builtin_popcountll(bs[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (((sel >> e) & 1u) && p < (uint32_t)k) {
+        oi[p] = i + e;
+        if (ov) ov[p] = v[e];
+        ++p;
+      }
+    }
+    pos += total;
+    eq_rank += eq_total;
+  });
+}
+
+}  // namespace
+
+hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
+                              const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
+                              int32_t batch, int32_t next_n, int32_t workers, int32_t k,
+                              int32_t* out_idx, float* out_val, int64_t ldk,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(select_topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, logits, ldo,
+                     max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
+                     ldk);
+  return hipGetLastError();
+}
+
+}  // namespace pmqa

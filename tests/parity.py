@@ -35,3 +35,32 @@ def check(gpu, ref, label=""):
         raise AssertionError(f"{label}: {int(over.sum())} entries outside tolerance: {details}")
     ratio = float((err[unmasked] / tol[unmasked]).max()) if unmasked.any() else 0.0
     return {"masked": int(masked.sum()), "checked": int(unmasked.sum()), "max_err_over_tol": ratio}
+
+
+def check_topk(idx, val, ref, n_rows, k, label=""):
+    """Top-k of GPU rows against the fp64 oracle.
+
+    idx, val: GPU output [rows, k]; ref: oracle dict of those rows (logits,
+    tol); n_rows: candidate count per row.  Checks the layout (ascending
+    columns below n, then -1 / -inf), each value within tolerance of the
+    oracle, and that the selection is one a tie-aware reader of the oracle
+    could make: no unselected candidate exceeds a selected one by more than
+    their two tolerances."""
+    want, tol = ref["logits"], ref["tol"]
+    for r in range(idx.shape[0]):
+        n = int(n_rows[r])
+        cnt = min(k, n)
+        sel = idx[r, :cnt].astype(np.int64)
+        assert np.all(idx[r, cnt:] == -1) and np.all(np.isneginf(val[r, cnt:])), (label, r)
+        assert np.all(np.diff(sel) > 0) and (cnt == 0 or (sel[0] >= 0 and sel[-1] < n)), \
+            (label, r)
+        if cnt == 0:
+            continue
+        assert np.all(np.abs(val[r, :cnt].astype(np.float64) - want[r, sel]) <= tol[r, sel]), \
+            (label, r)
+        if cnt < n:
+            mask = np.ones(n, bool)
+            mask[sel] = False
+            lo = np.min(want[r, sel] + tol[r, sel])
+            hi = np.max(want[r, :n][mask] - tol[r, :n][mask])
+            assert hi <= lo, (label, r, hi, lo)
