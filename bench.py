@@ -159,7 +159,8 @@ def describe(cfg):
     else:
         dist = f"ctx uniform [{cfg.ctx_lo}, {cfg.ctx_hi}]"
     zeros = f", {cfg.zero_frac:.0%} empty rows" if cfg.zero_frac else ""
-    return (f"{cfg.name}: B={cfg.batch} decode, next_n={cfg.next_n}, {cfg.variant}, 64 heads, "
+    return (f"{cfg.name}: B={cfg.batch} decode, next_n={cfg.next_n}, {cfg.variant}, "
+            f"{cfg.num_heads} heads, "
             f"head_dim 128, 64-token pages, {dist}{zeros}, logits [{cfg.batch * cfg.next_n}, "
             f"{cfg.max_context_len}] fp32; step = graph replay of compute_schedule + "
             f"paged_mqa_logits_{cfg.variant}")
@@ -201,7 +202,8 @@ def main():
     torch.cuda.set_device(0)
     keys = ("q", "kv_cache", "weights", "context_lens", "block_table") + (() if fp8 else ("q_scale",))
     dev = {k: torch.from_numpy(np.ascontiguousarray(data[k])).cuda() for k in keys}
-    W = pmqa.default_num_workers(variant, NN)
+    H = int(data["q"].shape[2])
+    W = pmqa.default_num_workers(variant, NN, num_heads=H)
     sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
     out = torch.empty((B * NN, M), dtype=torch.float32, device="cuda")
 
@@ -333,7 +335,7 @@ def main():
 
     tokens = scored_tokens(ctx_np, NN, M)
     sbytes = pmqa.schedule_bytes(B, W)
-    alg = algorithmic_bytes(ctx_np, NN, M, pmqa.NUM_HEADS, pmqa.HEAD_DIM, pmqa.PAGE_SIZE, sbytes,
+    alg = algorithmic_bytes(ctx_np, NN, M, H, pmqa.HEAD_DIM, pmqa.PAGE_SIZE, sbytes,
                             data["variant"])
     achieved = alg / (k_mean * 1e-3) / 1e9
     src_hash = kernel_source_hash()
@@ -372,7 +374,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
-                                f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}>"),
+                                f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
                      "kernel_source_hash": src_hash},
         "sampled_parity": ok,
         "cpu_baseline": cpu,

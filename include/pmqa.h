@@ -28,9 +28,9 @@
  *  - No C++ exception crosses the ABI.  Every call returns a pmqa_status_t;
  *    pmqa_last_error() returns a message naming the offending argument.
  *  - Always-on checks cost O(1) host work: null pointers, alignment, sizes,
- *    strides, the compiled specialisation (num_heads 64, head_dim 128,
- *    page_size 64, next_n 1 or 2) and, once per device, that the device is a
- *    gfx950.
+ *    strides, the compiled specialisation (num_heads 64, 32 or 16, head_dim
+ *    128, page_size 64, next_n 1 or 2) and, once per device, that the device
+ *    is a gfx950.
  *  - Validate mode (environment variable PMQA_VALIDATE_INPUTS=1, read on
  *    every call) adds checks of device contents: context lengths, the used
  *    block-table entries and the schedule's freshness.  They copy data to the
@@ -82,10 +82,11 @@ const char* pmqa_last_error(void);
 
 /* Persistent-grid size for a logits kernel on `device`: compute units times
  * the kernel's resident workgroups per compute unit times 4 wavefronts per
- * workgroup (one worker = one wavefront).  Host-only query; writes the count
- * to *num_workers (host pointer). */
+ * workgroup (one worker = one wavefront).  The kernel, and so its
+ * occupancy, depends on variant, next_n and num_heads (64, 32 or 16).
+ * Host-only query; writes the count to *num_workers (host pointer). */
 pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next_n,
-                                       int32_t* num_workers);
+                                       int32_t num_heads, int32_t* num_workers);
 
 /* Bytes of a schedule buffer for `batch` rows and `num_workers` workers:
  * 4 * (8 + 2*(num_workers+1) + batch + 1).  Returns 0 for invalid sizes. */
@@ -166,13 +167,15 @@ pmqa_status_t refresh_schedule(const int32_t* context_lens, int32_t batch, int32
  * paged_mqa_logits_fp8 - logits from an fp8 paged K cache.
  *
  * Page: introduction (fp8 kernel, weighted sum of rectified scores) and
- * section 1 (zero-length rows skipped by the task iterator).
+ * section 1 (zero-length rows skipped by the task iterator; an epilogue
+ * sized by num_heads).
  *
- *   q             e4m3fn [batch, next_n, 64, 128], contiguous, 16-B aligned.
+ *   q             e4m3fn [batch, next_n, H, 128], contiguous, 16-B aligned
+ *                 (H = num_heads).
  *   kv_cache      uint8 [num_pages][8448], 16-B aligned: per page 64 tokens x
  *                 128 e4m3fn bytes (token-major), then 64 little-endian fp32
  *                 per-token scales.  Only pages of tokens t < ctx_b are read.
- *   weights       fp32 [batch*next_n, 64], contiguous, 16-B aligned.
+ *   weights       fp32 [batch*next_n, H], contiguous, 16-B aligned.
  *   context_lens  int32 [batch].
  *   block_table   int32 [batch, block_table_stride]; entry i of row b names
  *                 the physical page of tokens [64i, 64i+64).  Only entries
@@ -184,7 +187,7 @@ pmqa_status_t refresh_schedule(const int32_t* context_lens, int32_t batch, int32
  *                 scores for t < min(ctx_b - next_n + 1 + j, max_context_len)
  *                 and -inf for the rest (tokens >= max_context_len are
  *                 truncated).  Columns >= max_context_len are not touched.
- *   num_heads 64, head_dim 128, page_size 64, next_n 1 or 2 (else
+ *   num_heads 64, 32 or 16, head_dim 128, page_size 64, next_n 1 or 2 (else
  *   PMQA_ERR_UNSUPPORTED); num_pages >= 1; block_table_stride >= 1;
  *   max_context_len >= 1.
  */
@@ -204,9 +207,9 @@ pmqa_status_t paged_mqa_logits_fp8(const void* q, const void* kv_cache, const fl
  * one E8M0 scale per 32 consecutive elements along head_dim; there is no
  * per-token fp32 scale (scale_t = 1).
  *
- *   q             packed e2m1 [batch, next_n, 64, 64] (element 2i in the low
+ *   q             packed e2m1 [batch, next_n, H, 64] (element 2i in the low
  *                 nibble of byte i), 16-B aligned.
- *   q_scale       e8m0 [batch, next_n, 64, 4] (no alignment requirement).
+ *   q_scale       e8m0 [batch, next_n, H, 4] (no alignment requirement).
  *   kv_cache      uint8 [num_pages][4352], 16-B aligned: 64 tokens x 64 packed
  *                 bytes (token-major), then 64 tokens x 4 e8m0 block scales.
  *   All other arguments as for paged_mqa_logits_fp8.

@@ -75,7 +75,7 @@ _lib.pmqa_last_error.argtypes = []
 _lib.pmqa_schedule_bytes.restype = ctypes.c_size_t
 _lib.pmqa_schedule_bytes.argtypes = [_i32, _i32]
 _lib.pmqa_default_num_workers.restype = ctypes.c_int
-_lib.pmqa_default_num_workers.argtypes = [ctypes.c_int, _i32, _i32, ctypes.POINTER(_i32)]
+_lib.pmqa_default_num_workers.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_i32)]
 _lib.compute_schedule.restype = ctypes.c_int
 _lib.compute_schedule.argtypes = [_p, _i32, _i32, _p, _p]
 _lib.compute_schedule_linear.restype = ctypes.c_int
@@ -145,17 +145,19 @@ def schedule_bytes(batch, num_workers):
     return int(_lib.pmqa_schedule_bytes(int(batch), int(num_workers)))
 
 
-def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None):
+def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None, num_heads=NUM_HEADS):
     dev = torch.cuda.current_device() if device is None else int(device)
     out = _i32(0)
-    _check(_lib.pmqa_default_num_workers(dev, int(variant), int(next_n), ctypes.byref(out)))
+    _check(_lib.pmqa_default_num_workers(dev, int(variant), int(next_n), int(num_heads),
+                                         ctypes.byref(out)))
     return int(out.value)
 
 
-def _schedule_buffer(context_lens, num_workers, out, variant, next_n):
+def _schedule_buffer(context_lens, num_workers, out, variant, next_n, num_heads=NUM_HEADS):
     _need(context_lens, "context_lens", (torch.int32,), ndim=1)
     B = context_lens.shape[0]
-    W = default_num_workers(variant, next_n) if num_workers is None else int(num_workers)
+    W = (default_num_workers(variant, next_n, num_heads=num_heads) if num_workers is None
+         else int(num_workers))
     words = schedule_bytes(B, W) // 4
     if out is None:
         out = torch.empty(words, dtype=torch.int32, device=context_lens.device)
@@ -167,9 +169,11 @@ def _schedule_buffer(context_lens, num_workers, out, variant, next_n):
 
 
 def compute_schedule(context_lens, num_workers=None, out=None, variant=VARIANT_FP8, next_n=1,
-                     stream=None):
-    """Schedule (int32 tensor) of the persistent workers for these lengths."""
-    B, W, out = _schedule_buffer(context_lens, num_workers, out, variant, next_n)
+                     stream=None, num_heads=NUM_HEADS):
+    """Schedule (int32 tensor) of the persistent workers for these lengths
+    (default worker count: that of the logits kernel for variant, next_n and
+    num_heads)."""
+    B, W, out = _schedule_buffer(context_lens, num_workers, out, variant, next_n, num_heads)
     _check(_lib.compute_schedule(_ptr(context_lens), B, W, _ptr(out), _stream_ptr(stream)))
     return out
 

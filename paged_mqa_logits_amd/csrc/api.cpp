@@ -83,9 +83,11 @@ struct Shape {
 
 pmqa_status_t check_shape(const Shape& s, int32_t num_heads, int32_t head_dim, int32_t page_size) {
   if (s.batch < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "batch = %d must be >= 1", s.batch);
-  if (num_heads != pmqa::kHeads || head_dim != pmqa::kHeadDim || page_size != pmqa::kPage)
+  if ((num_heads != 64 && num_heads != 32 && num_heads != 16) || head_dim != pmqa::kHeadDim ||
+      page_size != pmqa::kPage)
     return fail(PMQA_ERR_UNSUPPORTED,
-                "(num_heads, head_dim, page_size) = (%d, %d, %d) not compiled; only (64, 128, 64)",
+                "(num_heads, head_dim, page_size) = (%d, %d, %d) not compiled; only "
+                "(64, 32 or 16, 128, 64)",
                 num_heads, head_dim, page_size);
   if (s.next_n != 1 && s.next_n != 2)
     return fail(PMQA_ERR_UNSUPPORTED, "next_n = %d not compiled; only 1 or 2", s.next_n);
@@ -215,8 +217,8 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
                                   g_cus[dev].load(std::memory_order_acquire), stream);
     if (e != hipSuccess) return fail(PMQA_ERR_HIP, "-inf fill launch: %s", hipGetErrorString(e));
   }
-  e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, stream)
-                                  : pmqa::launch_logits_fp4(a, s.next_n, stream);
+  e = variant == PMQA_VARIANT_FP8 ? pmqa::launch_logits_fp8(a, s.next_n, num_heads, stream)
+                                  : pmqa::launch_logits_fp4(a, s.next_n, num_heads, stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -233,12 +235,15 @@ size_t pmqa_schedule_bytes(int32_t batch, int32_t num_workers) {
 }
 
 pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next_n,
-                                       int32_t* num_workers) {
+                                       int32_t num_heads, int32_t* num_workers) {
   if (!num_workers) return fail(PMQA_ERR_INVALID_ARGUMENT, "num_workers is null");
   if (variant != PMQA_VARIANT_FP8 && variant != PMQA_VARIANT_FP4)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "variant = %d is not fp8 (0) or fp4 (1)", variant);
   if (next_n != 1 && next_n != 2)
     return fail(PMQA_ERR_UNSUPPORTED, "next_n = %d not compiled; only 1 or 2", next_n);
+  if (num_heads != 64 && num_heads != 32 && num_heads != 16)
+    return fail(PMQA_ERR_UNSUPPORTED, "num_heads = %d not compiled; only 64, 32 or 16",
+                num_heads);
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -250,7 +255,7 @@ pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next
   int cus = 0, blocks = 0;
   if (st == PMQA_OK) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-    if (e == hipSuccess) e = pmqa::logits_blocks_per_cu(variant, next_n, &blocks);
+    if (e == hipSuccess) e = pmqa::logits_blocks_per_cu(variant, next_n, num_heads, &blocks);
     if (e != hipSuccess) st = fail(PMQA_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
   }
   if (device != cur) hipSetDevice(cur);

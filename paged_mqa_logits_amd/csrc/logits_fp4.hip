@@ -5,13 +5,13 @@
 
 namespace pmqa {
 
-hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream) {
-  return launch_logits<Fp4Format>(a, next_n, stream);
+hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, int heads, hipStream_t stream) {
+  return launch_logits<Fp4Format>(a, next_n, heads, stream);
 }
 
-hipError_t logits_blocks_per_cu(int variant, int next_n, int* blocks) {
-  return variant == 0 ? blocks_per_cu<Fp8Format>(next_n, blocks)
-                      : blocks_per_cu<Fp4Format>(next_n, blocks);
+hipError_t logits_blocks_per_cu(int variant, int next_n, int heads, int* blocks) {
+  return variant == 0 ? blocks_per_cu<Fp8Format>(next_n, heads, blocks)
+                      : blocks_per_cu<Fp4Format>(next_n, heads, blocks);
 }
 
 }  // namespace pmqa

@@ -5,8 +5,8 @@
 
 namespace pmqa {
 
-hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, hipStream_t stream) {
-  return launch_logits<Fp8Format>(a, next_n, stream);
+hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, int heads, hipStream_t stream) {
+  return launch_logits<Fp8Format>(a, next_n, heads, stream);
 }
 
 }  // namespace pmqa

@@ -211,9 +211,12 @@ struct Fp8Format {
   static constexpr bool kTokenScale = true;
   static constexpr int kLdsBytes = kPage * kHeadDim;  // transpose buffer per wave
   // Waves per SIMD (one: the stream is memory-bound and the registers go to
-  // the K ring) and units of logits staged per wave.
-  static constexpr int waves_per_simd(int) { return 1; }
-  static constexpr int stage_units(int nn) { return 28 / nn; }
+  // the K ring) and units of logits staged per wave.  With 32 or 16 heads
+  // the smaller query block and accumulators would let two waves fit, but
+  // that halves the stage (two workgroups in LDS), and measured on MI355X
+  // the longer write bursts of one wave per SIMD win.
+  static constexpr int waves_per_simd(int, int) { return 1; }
+  static constexpr int stage_units(int nn, int) { return 28 / nn; }
   struct KFrag {
     v4i raw[8];  // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
     float s;     // scale of token `lane` of the page
@@ -221,9 +224,9 @@ struct Fp8Format {
   struct KOp {
     v8i k[4];    // MFMA B operand of token group tg
   };
-  template <int NN>
+  template <int NN, int HG>
   struct QFrag {
-    v8i q[NN][4];
+    v8i q[NN][HG];
   };
   __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
 #pragma unroll
@@ -254,24 +257,24 @@ struct Fp8Format {
       o.k[tg] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
-  template <int NN>
+  template <int NN, int HG>
   __device__ __forceinline__ static void load_q(const LogitsArgs& a, int32_t b, int lane,
-                                                QFrag<NN>& q) {
+                                                QFrag<NN, HG>& q) {
     const int c = lane >> 4, tl = lane & 15;
 #pragma unroll
     for (int j = 0; j < NN; ++j)
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) {
-        const int64_t row = ((int64_t)b * NN + j) * kHeads + 16 * hg + tl;
+      for (int hg = 0; hg < HG; ++hg) {
+        const int64_t row = ((int64_t)b * NN + j) * (16 * HG) + 16 * hg + tl;
         const v4i* src = reinterpret_cast<const v4i*>(a.q + row * kHeadDim + 32 * c);
         const v4i lo = src[0];
         const v4i hi = src[1];
         q.q[j][hg] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
   }
-  template <int NN>
-  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& o,
-                                            int tg) {
+  template <int NN, int HG>
+  __device__ __forceinline__ static v4f mma(const QFrag<NN, HG>& q, int j, int hg,
+                                            const KOp& o, int tg) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.q[j][hg], o.k[tg], zero, kFmtFp8,
                                                             kFmtFp8, 0, kScaleOne, 0, kScaleOne);
@@ -295,8 +298,8 @@ struct Fp4Format {
   // Two waves per SIMD (a page costs as many MFMA and VALU issues as an fp8
   // page for half the bytes, so a second wave fills the issue gaps of the
   // first), with the logits stage halved to fit two workgroups in LDS.
-  static constexpr int waves_per_simd(int) { return 2; }
-  static constexpr int stage_units(int nn) { return 14 / nn; }
+  static constexpr int waves_per_simd(int, int) { return 2; }
+  static constexpr int stage_units(int nn, int) { return 14 / nn; }
   struct KFrag {
     v4i raw[4];   // raw[i]: bytes [1024 i + 16 lane, +16) of the page's values
     int32_t sc;   // the 4 E8M0 block scales of token `lane`
@@ -305,10 +308,10 @@ struct Fp4Format {
     v4i k[4];     // B operand of token group tg (16 bytes = 32 elements)
     int32_t sc[4];
   };
-  template <int NN>
+  template <int NN, int HG>
   struct QFrag {
-    v4i q[NN][4];
-    int32_t sc[NN][4];
+    v4i q[NN][HG];
+    int32_t sc[NN][HG];
   };
   __device__ __forceinline__ static void load_k(rsrc_t pg, int lane, KFrag& f) {
 #pragma unroll
@@ -333,22 +336,22 @@ struct Fp4Format {
       o.sc[tg] = (owner >> (8 * c)) & 0xFF;
     }
   }
-  template <int NN>
+  template <int NN, int HG>
   __device__ __forceinline__ static void load_q(const LogitsArgs& a, int32_t b, int lane,
-                                                QFrag<NN>& q) {
+                                                QFrag<NN, HG>& q) {
     const int c = lane >> 4, tl = lane & 15;
 #pragma unroll
     for (int j = 0; j < NN; ++j)
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) {
-        const int64_t row = ((int64_t)b * NN + j) * kHeads + 16 * hg + tl;
+      for (int hg = 0; hg < HG; ++hg) {
+        const int64_t row = ((int64_t)b * NN + j) * (16 * HG) + 16 * hg + tl;
         q.q[j][hg] = *reinterpret_cast<const v4i*>(a.q + row * (kHeadDim / 2) + 16 * c);
         q.sc[j][hg] = a.q_scale[row * (kHeadDim / 32) + c];
       }
   }
-  template <int NN>
-  __device__ __forceinline__ static v4f mma(const QFrag<NN>& q, int j, int hg, const KOp& o,
-                                            int tg) {
+  template <int NN, int HG>
+  __device__ __forceinline__ static v4f mma(const QFrag<NN, HG>& q, int j, int hg,
+                                            const KOp& o, int tg) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const v4i x = q.q[j][hg];
     const v4i y = o.k[tg];
@@ -359,25 +362,26 @@ struct Fp4Format {
   }
 };
 
-// Per-row operands held in registers while a worker stays on one batch row.
-template <class Fmt, int NN>
+// Per-row operands held in registers while a worker stays on one batch row
+// (HG groups of 16 heads).
+template <class Fmt, int NN, int HG>
 struct RowState {
-  typename Fmt::template QFrag<NN> q;
-  v4f w[NN][4];  // weights of heads 16*hg + 4*(lane>>4) + i
+  typename Fmt::template QFrag<NN, HG> q;
+  v4f w[NN][HG];  // weights of heads 16*hg + 4*(lane>>4) + i
   int32_t b;
 };
 
-template <class Fmt, int NN>
+template <class Fmt, int NN, int HG>
 __device__ __forceinline__ void load_row(const LogitsArgs& a, int32_t b, int lane,
-                                         RowState<Fmt, NN>& rs) {
-  Fmt::template load_q<NN>(a, b, lane, rs.q);
+                                         RowState<Fmt, NN, HG>& rs) {
+  Fmt::template load_q<NN, HG>(a, b, lane, rs.q);
   const int c = lane >> 4;
 #pragma unroll
   for (int j = 0; j < NN; ++j)
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg)
-      rs.w[j][hg] = *reinterpret_cast<const v4f*>(a.weights + ((int64_t)b * NN + j) * kHeads +
-                                                  16 * hg + 4 * c);
+    for (int hg = 0; hg < HG; ++hg)
+      rs.w[j][hg] = *reinterpret_cast<const v4f*>(
+          a.weights + ((int64_t)b * NN + j) * (16 * HG) + 16 * hg + 4 * c);
   rs.b = b;
 }
 
@@ -394,9 +398,9 @@ __device__ __forceinline__ void load_page(const LogitsArgs& a, const Unit& t, in
 // Contract page p of unit t against every query row of the batch row and
 // apply the epilogue; lane l returns the logit of token l of the page for
 // each query row (-inf past the row's causal limit).
-template <class Fmt, int NN>
+template <class Fmt, int NN, int HG>
 __device__ __forceinline__ void process_page(const Unit& t, int p, const typename Fmt::KFrag& f,
-                                             uint8_t* lds, const RowState<Fmt, NN>& rs,
+                                             uint8_t* lds, const RowState<Fmt, NN, HG>& rs,
                                              const LogitsArgs& a, int32_t rows, int lane,
                                              float (&res)[NN]) {
   const int32_t tok = t.u * kUnit + p * kPage + lane;
@@ -421,16 +425,17 @@ __device__ __forceinline__ void process_page(const Unit& t, int p, const typenam
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const float bnd = ((neg >> (16 * tg + tl)) & 1) ? ninf : pos;
-      v4f acc[NN][4];
+      v4f acc[NN][HG];
 #pragma unroll
       for (int j = 0; j < NN; ++j)
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) acc[j][hg] = Fmt::template mma<NN>(rs.q, j, hg, op, tg);
+        for (int hg = 0; hg < HG; ++hg)
+          acc[j][hg] = Fmt::template mma<NN, HG>(rs.q, j, hg, op, tg);
 #pragma unroll
       for (int j = 0; j < NN; ++j) {
         float sum = 0.f;
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg)
+        for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sum = __builtin_fmaf(rs.w[j][hg][i], __builtin_amdgcn_fmed3f(acc[j][hg][i], 0.f, bnd),
@@ -463,9 +468,9 @@ __device__ __forceinline__ int32_t xcd_block(int32_t bid, int32_t nblk) {
 // Writing in a few large bursts instead of 256 bytes after every page keeps
 // most of the output traffic out of the read stream.  The stage takes what
 // LDS is left once the format's workgroups per compute unit are resident.
-template <class Fmt, int NN>
+template <class Fmt, int NN, int HG>
 struct Stage {
-  static constexpr int kUnits = Fmt::stage_units(NN);
+  static constexpr int kUnits = Fmt::stage_units(NN, HG);
   static constexpr int kFloats = kUnits * NN * kUnit;
 };
 
@@ -494,12 +499,12 @@ __device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* st
   }
 }
 
-template <class Fmt, int NN>
+template <class Fmt, int NN, int HG>
 __global__ __launch_bounds__(kBlockThreads)
-__attribute__((amdgpu_waves_per_eu(Fmt::waves_per_simd(NN), Fmt::waves_per_simd(NN))))
+__attribute__((amdgpu_waves_per_eu(Fmt::waves_per_simd(NN, HG), Fmt::waves_per_simd(NN, HG))))
 void logits_kernel(const LogitsArgs a) {
-  __shared__ float stage_all[kWavesPerBlock][Stage<Fmt, NN>::kFloats];
-  __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<Fmt, NN>::kUnits];
+  __shared__ float stage_all[kWavesPerBlock][Stage<Fmt, NN, HG>::kFloats];
+  __shared__ int32_t meta_all[kWavesPerBlock][2 * Stage<Fmt, NN, HG>::kUnits];
   __shared__ __attribute__((aligned(16))) uint8_t xpose_all[kWavesPerBlock][Fmt::kLdsBytes > 0 ? Fmt::kLdsBytes : 16];
   const int lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -523,7 +528,7 @@ void logits_kernel(const LogitsArgs a) {
   typename Fmt::KFrag ring[kPagesPerUnit];
 #pragma unroll
   for (int p = 0; p < kPagesPerUnit; ++p) load_page<Fmt>(a, cur, p, rows, lane, ring[p]);
-  RowState<Fmt, NN> rs;
+  RowState<Fmt, NN, HG> rs;
   rs.b = -1;
   int32_t staged = 0;
   // One exit, after the flush of the last unit, so the load counter has the
@@ -531,7 +536,7 @@ void logits_kernel(const LogitsArgs a) {
   // for its own loads.
   while (true) {
     if (cur.b != rs.b) {  // new batch row: its query block and weights
-      load_row<Fmt, NN>(a, cur.b, lane, rs);
+      load_row<Fmt, NN, HG>(a, cur.b, lane, rs);
       __builtin_amdgcn_s_waitcnt(0);
     }
     const Unit nxt = it.next(cur);  // lookahead: same iterator as the consumer
@@ -539,7 +544,7 @@ void logits_kernel(const LogitsArgs a) {
 #pragma unroll
     for (int p = 0; p < kPagesPerUnit; ++p) {
       float res[NN];
-      process_page<Fmt, NN>(cur, p, ring[p], xpose, rs, a, rows, lane, res);
+      process_page<Fmt, NN, HG>(cur, p, ring[p], xpose, rs, a, rows, lane, res);
       load_page<Fmt>(a, nxt, p, rows, lane, ring[p]);
 #pragma unroll
       for (int j = 0; j < NN; ++j) dst[j * kUnit + p * kPage + lane] = res[j];
@@ -550,7 +555,7 @@ void logits_kernel(const LogitsArgs a) {
     }
     ++staged;
     const bool last = !it.valid(nxt);
-    if (staged == Stage<Fmt, NN>::kUnits || last) {
+    if (staged == Stage<Fmt, NN, HG>::kUnits || last) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       flush_stage<NN>(a, stage, meta, staged, lane);
@@ -562,24 +567,38 @@ void logits_kernel(const LogitsArgs a) {
   }
 }
 
-template <class Fmt>
-hipError_t launch_logits(const LogitsArgs& a, int next_n, hipStream_t stream) {
+template <class Fmt, int NN, int HG>
+hipError_t launch_one(const LogitsArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_workers + kWavesPerBlock - 1) / kWavesPerBlock);
-  const dim3 block(kBlockThreads);
-  if (next_n == 1)
-    hipLaunchKernelGGL((logits_kernel<Fmt, 1>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((logits_kernel<Fmt, 2>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((logits_kernel<Fmt, NN, HG>), grid, dim3(kBlockThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+// heads: 64, 32 or 16 (checked by the caller).
 template <class Fmt>
-hipError_t blocks_per_cu(int next_n, int* blocks) {
+hipError_t launch_logits(const LogitsArgs& a, int next_n, int heads, hipStream_t stream) {
   if (next_n == 1)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, logits_kernel<Fmt, 1>,
-                                                        kBlockThreads, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, logits_kernel<Fmt, 2>,
+    return heads == 64 ? launch_one<Fmt, 1, 4>(a, stream)
+                       : heads == 32 ? launch_one<Fmt, 1, 2>(a, stream)
+                                     : launch_one<Fmt, 1, 1>(a, stream);
+  return heads == 64 ? launch_one<Fmt, 2, 4>(a, stream)
+                     : heads == 32 ? launch_one<Fmt, 2, 2>(a, stream)
+                                   : launch_one<Fmt, 2, 1>(a, stream);
+}
+
+template <class Fmt, int NN, int HG>
+hipError_t occupancy(int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, logits_kernel<Fmt, NN, HG>,
                                                       kBlockThreads, 0);
+}
+
+template <class Fmt>
+hipError_t blocks_per_cu(int next_n, int heads, int* blocks) {
+  if (next_n == 1)
+    return heads == 64 ? occupancy<Fmt, 1, 4>(blocks)
+                       : heads == 32 ? occupancy<Fmt, 1, 2>(blocks) : occupancy<Fmt, 1, 1>(blocks);
+  return heads == 64 ? occupancy<Fmt, 2, 4>(blocks)
+                     : heads == 32 ? occupancy<Fmt, 2, 2>(blocks) : occupancy<Fmt, 2, 1>(blocks);
 }
 
 }  // namespace pmqa

@@ -8,7 +8,7 @@
 
 namespace pmqa {
 
-constexpr int kHeads = 64;
+constexpr int kHeads = 64;  // the most heads a query row may have (also 32 or 16)
 constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
 constexpr int kUnit = 256;
@@ -46,8 +46,9 @@ hipError_t launch_schedule(const int32_t* ctx, int32_t batch, int32_t num_worker
 // Rebuilds sched only when it does not match (batch, num_workers, ctx).
 hipError_t launch_refresh_schedule(const int32_t* ctx, int32_t batch, int32_t num_workers,
                                    int32_t* sched, int32_t* recomputed, hipStream_t stream);
-hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, hipStream_t stream);
-hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, hipStream_t stream);
+// heads: 64, 32 or 16.
+hipError_t launch_logits_fp8(const LogitsArgs& a, int next_n, int heads, hipStream_t stream);
+hipError_t launch_logits_fp4(const LogitsArgs& a, int next_n, int heads, hipStream_t stream);
 // -inf over columns [0, max_ctx) of every output row (runs before the unit
 // kernel, which overwrites the scheduled units).
 hipError_t launch_neg_inf_fill(float* out, int64_t ldo, int64_t rows, int32_t max_ctx,
@@ -73,6 +74,6 @@ hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, in
                               int32_t* out_idx, float* out_val, int64_t ldk, hipStream_t stream);
 
 // Resident workgroups per compute unit of a logits kernel (occupancy query).
-hipError_t logits_blocks_per_cu(int variant, int next_n, int* blocks);
+hipError_t logits_blocks_per_cu(int variant, int next_n, int heads, int* blocks);
 
 }  // namespace pmqa

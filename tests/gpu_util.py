@@ -34,7 +34,8 @@ def run(data, dev=None, num_workers=None, out=None, schedule=None):
     nn = int(data["next_n"])
     if schedule is None:
         schedule = pmqa.compute_schedule(dev["context_lens"], num_workers=num_workers,
-                                         variant=variant, next_n=nn)
+                                         variant=variant, next_n=nn,
+                                         num_heads=int(data["q"].shape[2]))
     M = int(data["max_context_len"])
     if out is None:
         out = poisoned_out(len(data["context_lens"]) * nn, M)

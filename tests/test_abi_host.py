@@ -68,7 +68,7 @@ def _fp8(lib, **kw):
     (dict(out=FAKE + 8), 1, "logits must be 16-byte aligned"),
     (dict(ctx=FAKE + 2), 1, "4-byte aligned"),
     (dict(batch=0), 1, "batch"),
-    (dict(heads=32), 2, "not compiled"),
+    (dict(heads=48), 2, "not compiled"),
     (dict(dim=64), 2, "not compiled"),
     (dict(page=16), 2, "not compiled"),
     (dict(next_n=3), 2, "next_n = 3"),
@@ -122,9 +122,10 @@ def test_refresh_schedule_flag_alignment():
 def test_default_num_workers_argument_checks():
     lib = pmqa.library()
     out = ctypes.c_int32(0)
-    assert lib.pmqa_default_num_workers(0, 5, 1, ctypes.byref(out)) == 1
-    assert lib.pmqa_default_num_workers(0, 0, 3, ctypes.byref(out)) == 2
-    assert lib.pmqa_default_num_workers(0, 0, 1, None) == 1
+    assert lib.pmqa_default_num_workers(0, 5, 1, 64, ctypes.byref(out)) == 1
+    assert lib.pmqa_default_num_workers(0, 0, 3, 64, ctypes.byref(out)) == 2
+    assert lib.pmqa_default_num_workers(0, 0, 1, 48, ctypes.byref(out)) == 2
+    assert lib.pmqa_default_num_workers(0, 0, 1, 64, None) == 1
 
 
 def test_binding_rejects_cpu_tensors():

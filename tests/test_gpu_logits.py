@@ -139,6 +139,27 @@ def test_large_batch_of_short_rows():
     parity.check(lg, oracle(d), "batch 16385")
 
 
+@pytest.mark.parametrize("variant", ["fp8", "fp4"])
+@pytest.mark.parametrize("next_n", [1, 2])
+@pytest.mark.parametrize("heads", [32, 16])
+def test_fewer_heads(variant, next_n, heads):
+    """Query blocks of 32 and 16 heads (the kernels with 2 and 1 head groups)."""
+    announce(f"{variant} heads={heads} next_n={next_n}")
+    rng = np.random.default_rng(76 + heads + next_n)
+    ctx = rng.integers(0, 2500, size=30)
+    ctx[::7] = 0
+    ctx[1] = 1
+    ctx[2] = 2600                                   # truncated
+    mk = make_fp8 if variant == "fp8" else make_fp4
+    kw = dict(negative_scales=True) if variant == "fp8" else {}
+    d = mk(ctx, next_n=next_n, max_context_len=2500, seed=76 + heads, num_heads=heads,
+           bt_stride=-(-2600 // 64), **kw)
+    ref = oracle(d)
+    for W in (None, 7):
+        lg, _ = run(d, num_workers=W)
+        parity.check(lg, ref, f"{variant} H={heads} NN={next_n} W={W}")
+
+
 # ---------------------------------------------------------------- self-consistency
 
 def test_worker_count_invariance_and_determinism():
@@ -208,7 +229,7 @@ def _sample_rows(d, k, seed):
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name", ["large_fp8", "spec_fp8", "mxfp4"])
+@pytest.mark.parametrize("name", ["large_fp8", "spec_fp8", "mxfp4", "large_fp8_h16"])
 def test_full_size_config_sampled(name):
     """Full configuration in the launch configuration the benchmark times
     (default worker count); sampled rows against the oracle, and every row's

@@ -60,6 +60,7 @@ class WorkloadConfig:
     max_context_len: int = 0
     pool_factor: float = 1.2
     seed: int = 0
+    num_heads: int = 64
 
 
 CONFIGS = {
@@ -75,6 +76,13 @@ CONFIGS = {
                                max_context_len=131072, seed=3),
     "mxfp4": WorkloadConfig("mxfp4", "fp4", 512, 1, "uniform", 1024, 131072,
                             zero_frac=0.05, max_context_len=131072, seed=4),
+    # the large_fp8 lengths with query blocks of 32 and 16 heads
+    "large_fp8_h32": WorkloadConfig("large_fp8_h32", "fp8", 2048, 1, "lognormal", 1, 65536,
+                                    ctx_median=4096.0, ctx_sigma=1.0, zero_frac=0.10,
+                                    max_context_len=65536, seed=2, num_heads=32),
+    "large_fp8_h16": WorkloadConfig("large_fp8_h16", "fp8", 2048, 1, "lognormal", 1, 65536,
+                                    ctx_median=4096.0, ctx_sigma=1.0, zero_frac=0.10,
+                                    max_context_len=65536, seed=2, num_heads=16),
 }
 
 
@@ -284,6 +292,6 @@ def make_workload(cfg, **overrides):
     ctx = draw_context_lens(cfg, rng)
     maker = make_fp8 if cfg.variant == "fp8" else make_fp4
     data = maker(ctx, next_n=cfg.next_n, max_context_len=cfg.max_context_len,
-                 pool_factor=cfg.pool_factor, rng=rng)
+                 pool_factor=cfg.pool_factor, num_heads=cfg.num_heads, rng=rng)
     data["config"] = cfg
     return data
