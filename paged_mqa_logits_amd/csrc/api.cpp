@@ -211,6 +211,7 @@ pmqa_status_t logits_common(int variant, const void* q, const void* q_scale, con
   a.bt_stride = s.bt_stride;
   a.max_ctx = s.max_ctx;
   a.num_workers = s.workers;
+  a.flush_ticks = 1;  // replaced by the launcher
   hipError_t e = hipSuccess;
   if (fill) {
     e = pmqa::launch_neg_inf_fill(logits, s.ldo, (int64_t)s.batch * s.next_n, s.max_ctx,

@@ -36,6 +36,7 @@ struct LogitsArgs {
   int32_t bt_stride;
   int32_t max_ctx;
   int32_t num_workers;
+  uint32_t flush_ticks;     // period of the synchronised stage flushes (set by the launcher)
 };
 
 // Launchers (defined next to their kernels).  Return the launch status.
