@@ -29,6 +29,14 @@
 //      ballots.
 // Every pass reads 8 tiles ahead (8 16-byte reads in flight per lane for a
 // row in global memory; after the first pass they hit L2).
+//
+// Rows are taken longest first: a row's time grows with its candidate
+// count, and the dispatcher starts workgroups in index order, so workgroup i
+// selects for the row of rank i in decreasing candidate count (by a coarse
+// class: the top 3 bits of the count; ties by row index).  The longest rows
+// then start at once instead of whenever their index comes up.  Each
+// workgroup derives its row from the counts of all rows (for up to 8192
+// rows; beyond that workgroup i takes row i).
 #include <hip/hip_runtime.h>
 
 #include "pmqa_internal.h"
@@ -82,6 +90,18 @@ __device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
   }
   const int64_t lim = (int64_t)ctx[b] - next_n + 1 + j;
   return (int32_t)max((int64_t)0, min(min(lim, (int64_t)kUnit * c), (int64_t)max_ctx));
+}
+
+constexpr int kOrderRows = 8192;          // rows ordered longest first
+constexpr int kOrderBins = 128;           // count classes
+
+// Order-preserving coarse class of a candidate count: 0 for none, else
+// 1 + 4 floor(log2 n) + the two bits below the leading one (at most 124).
+__device__ __forceinline__ uint32_t count_class(int32_t n) {
+  if (n <= 0) return 0;
+  const int e = 31 - __builtin_clz((uint32_t)n);
+  const int m = e >= 2 ? (n >> (e - 2)) & 3 : (e == 1 ? (n & 1) << 1 : 0);
+  return 1u + 4u * (uint32_t)e + (uint32_t)m;
 }
 
 struct SelLds {
@@ -179,6 +199,69 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return x;
 }
 
+// The row of rank `rank` in decreasing count class (ties: lower row first);
+// rows <= kOrderRows.  Every thread calls it; LDS is free on return.
+__device__ __forceinline__ int32_t row_of_rank(SelLds& lds, int32_t rank, int32_t rows,
+                                            int32_t max_ctx, const int32_t* lengths,
+                                            const int32_t* ctx, const int32_t* sched,
+                                            int32_t batch, int32_t next_n, int32_t workers) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* cls = reinterpret_cast<uint8_t*>(lds.stage);  // class of each row
+  uint32_t* hist = lds.hist;
+  if (tid < kOrderBins) hist[tid] = 0;
+  __syncthreads();
+  for (int32_t q = tid; q < rows; q += kSelThreads) {
+    const uint32_t c =
+        count_class(row_candidates(q, max_ctx, lengths, ctx, sched, batch, next_n, workers));
+    cls[q] = (uint8_t)c;
+    atomicAdd(&hist[c], 1u);
+  }
+  __syncthreads();
+  // class holding the rank, counted from the top class down, and the rank
+  // of its first row
+  if (wave == 0) {
+    const uint32_t h0 = hist[kOrderBins - 1 - 2 * lane], h1 = hist[kOrderBins - 2 - 2 * lane];
+    const uint32_t own = h0 + h1;
+    uint32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const uint32_t above = incl - own, rk = (uint32_t)rank;
+    if (above <= rk && rk < above + h0) {
+      lds.chosen[0] = kOrderBins - 1 - 2 * lane;
+      lds.chosen[1] = above;
+    } else if (above + h0 <= rk && rk < incl) {
+      lds.chosen[0] = kOrderBins - 2 - 2 * lane;
+      lds.chosen[1] = above + h0;
+    }
+  }
+  __syncthreads();
+  const uint32_t want_cls = lds.chosen[0], j = (uint32_t)rank - lds.chosen[1];
+  // the j-th row of that class in row order, 512 rows per round
+  uint32_t base = 0;
+  for (int32_t r0 = 0; r0 < rows; r0 += kSelThreads) {
+    const int32_t q = r0 + tid;
+    const bool in = q < rows && cls[q] == want_cls;
+    const uint64_t m = __ballot(in);
+    if (lane == 0) lds.wave_sum[wave] = __builtin_popcountll(m);
+    __syncthreads();
+    uint32_t before = base, total = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      before += w < wave ? lds.wave_sum[w] : 0u;
+      total += lds.wave_sum[w];
+    }
+    if (in && before + lanes_below(m) == j) lds.chosen[2] = (uint32_t)q;
+    base += total;
+    __syncthreads();
+    if (base > j) break;  // uniform
+  }
+  const int32_t r = (int32_t)lds.chosen[2];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t max_ctx,
                         const int32_t* __restrict__ lengths, const int32_t* __restrict__ ctx,
@@ -188,7 +271,11 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
   __shared__ SelLds lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t r = blockIdx.x;
+  const int32_t rows = (int32_t)gridDim.x;
+  const int64_t r = rows <= kOrderRows
+                        ? row_of_rank(lds, (int32_t)blockIdx.x, rows, max_ctx, lengths, ctx,
+                                      sched, batch, next_n, workers)
+                        : (int64_t)blockIdx.x;
   const float* row = logits + r * ldo;
   int32_t* oi = out_idx + r * ldk;
   float* ov = out_val ? out_val + r * ldk : nullptr;
