@@ -18,6 +18,8 @@ Reported beside the step rate:
                 duration, against the 8 TB/s HBM peak; ``traffic`` is read from
                 the rocprofv3 counter summary in profiles/ when that summary was
                 taken on the current kernel sources, else null;
+  mfma_busy_pct the unit kernel's MFMA busy share from the committed
+                rocprofv3 counter summary (same rule), a secondary figure;
   cpu_baseline  the fp64 CPU oracle on a fixed subset of the same rows.
 """
 import argparse
@@ -36,6 +38,7 @@ METRIC = "KV tokens scored/s + achieved HBM GB/s, fp8 paged MQA logits, B=2048 d
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "large_fp8"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "logits_fp8_large_fp8_traffic.txt")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "logits_mfma_busy.txt")
 # Sources (under paged_mqa_logits_amd/) that determine the timed kernels,
 # compile flags included.
 KERNEL_SOURCES = ["csrc/logits_kernel.hpp", "csrc/logits_fp8.hip", "csrc/tail_fill.hip",
@@ -88,6 +91,24 @@ def read_traffic(expected_hash, launches_bytes):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_mfma_busy(expected_hash, workload):
+    """MFMA busy % of the workload's unit kernel from the committed counter
+    summary (a secondary figure), or None when it is missing or stale."""
+    if not os.path.exists(MFMA_SUMMARY):
+        return None
+    ok, val = False, None
+    with open(MFMA_SUMMARY) as f:
+        for line in f:
+            if line.startswith("# kernel source hash"):
+                ok = line.rsplit(":", 1)[1].strip() == expected_hash
+            elif not line.startswith("#") and line.startswith(workload + ","):
+                try:
+                    val = float(line.split(",")[3])
+                except (IndexError, ValueError):
+                    val = None
+    return val if ok else None
 
 
 def cpu_baseline(data, n_rows, seed):
@@ -376,6 +397,7 @@ def main():
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
                                 f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
                      "kernel_source_hash": src_hash},
+        "mfma_busy_pct": read_mfma_busy(src_hash, args.workload),
         "sampled_parity": ok,
         "cpu_baseline": cpu,
     }

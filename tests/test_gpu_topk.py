@@ -42,6 +42,26 @@ def test_select_topk_matches_oracle(pool, M, stride, k):
         assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
 
 
+@pytest.mark.parametrize("rows", [3000, 8192, 8193])
+def test_select_topk_many_rows(rows):
+    """Workgroups take rows longest first (by count class) up to 8192 rows,
+    in index order beyond: every row is still selected exactly once, with
+    lengths spread over many classes and many rows per class."""
+    announce(f"select_topk rows={rows}")
+    rng = np.random.default_rng(rows)
+    M, k = 300, 17
+    x = (rng.standard_normal((rows, M)) * 3).astype(np.float32)
+    n = rng.integers(0, M + 1, size=rows).astype(np.int32)
+    n[rng.random(rows) < 0.3] = 40                 # a crowded class
+    n[::97] = 0
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(rows):
+        wi, wv = otk.select_topk(x[r], int(n[r]), k)
+        assert np.array_equal(idx[r], wi), r
+        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+
+
 def test_select_topk_long_rows():
     announce("select_topk 131072 columns")
     rng = np.random.default_rng(9)
