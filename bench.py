@@ -20,6 +20,11 @@ Reported beside the step rate:
                 taken on the current kernel sources, else null;
   mfma_busy_pct the unit kernel's MFMA busy share from the committed
                 rocprofv3 counter summary (same rule), a secondary figure;
+  decode_drift  a graph of [every non-empty row += 1 token, refresh_schedule,
+                logits call] replayed step after step: the schedule is rebuilt
+                on the device whenever a row crosses a 256-token boundary;
+  copy_gbps     a plain 1 GiB device-to-device copy on the same box, read +
+                written bytes per second (frac_of_copy = achieved / it);
   cpu_baseline  the fp64 CPU oracle on a fixed subset of the same rows.
 """
 import argparse
@@ -137,7 +142,29 @@ def cpu_baseline(data, n_rows, seed):
     dt = time.perf_counter() - t0
     toks = scored_tokens(data["context_lens"][rows], nn, data["max_context_len"])
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{len(rows)} of {B} rows (seeded), {toks} KV tokens, {dt:.1f} s"}
+            "sample": f"{len(rows)} of {B} rows (seeded), {toks} KV tokens, {dt:.1f} s",
+            "cpu": cpu_model(), "blas": blas_name()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_name():
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        return ", ".join(libs) or None
+    except Exception:
+        return None
 
 
 def measure_append(pmqa, torch, batch, reps=20):
@@ -330,6 +357,59 @@ def main():
                 lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val),
                 args.steps), 2)}
 
+    # decode drift: every non-empty row grows by one token per step, so rows
+    # cross 256-token boundaries as decoding goes on; the graph refreshes the
+    # schedule on the device (rebuilding it when a unit count changed) before
+    # the logits call
+    ctx_d = dev["context_lens"].clone()
+    grow = (ctx_d > 0).to(torch.int32)
+    sched_d = torch.empty_like(sched)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rebuilds = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pmqa.compute_schedule(ctx_d, num_workers=W, out=sched_d)
+
+    def drift_step():
+        ctx_d.add_(grow)
+        pmqa.refresh_schedule(ctx_d, sched_d, num_workers=W, recomputed=flag)
+        if fp8:
+            pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], ctx_d,
+                                      dev["block_table"], sched_d, M, out=ws, num_workers=W)
+        else:
+            pmqa.paged_mqa_logits_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
+                                      ctx_d, dev["block_table"], sched_d, M, out=ws,
+                                      num_workers=W)
+        rebuilds.add_(flag)
+
+    torch.cuda.synchronize()
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(dgraph, stream=cap):
+            drift_step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    rebuilds.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        dgraph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    drift = {"steps": args.steps, "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 1),
+             "schedule_rebuilds": int(rebuilds.item())}
+    del dgraph
+
+    # a plain device-to-device copy of 1 GiB on the same box (bytes read + written)
+    src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+    del src, dst
+
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -385,10 +465,14 @@ def main():
             "batch": B, "next_n": NN, "max_context_len": M, "kv_tokens_per_step": tokens,
             "num_workers": W, "graph": True,
         },
+        "unique_kv_tokens_per_s": (int(np.clip(ctx_np.astype(np.int64), 0, M).sum()) /
+                                   (ms_step * 1e-3)) if NN > 1 else None,
         "gbps": alg / (ms_step * 1e-3) / 1e9,
         "algorithmic_bytes_per_step": alg,
-        "logits_call_us": {"mean": k_mean * 1e3, "p10": float(np.percentile(k_ms, 10)) * 1e3,
+        "logits_call_us": {"mean": k_mean * 1e3, "median": float(np.median(k_ms)) * 1e3,
+                             "p10": float(np.percentile(k_ms, 10)) * 1e3,
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
+        "decode_drift": drift,
         "schedule_us": {k: round(v, 2) for k, v in sched_us.items()},
         "append": append,
         "topk": topk,
@@ -396,7 +480,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
                                 f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
-                     "kernel_source_hash": src_hash},
+                     "kernel_source_hash": src_hash,
+                     "copy_gbps": copy_gbps,
+                     "frac_of_copy": achieved / copy_gbps if copy_gbps else None},
         "mfma_busy_pct": read_mfma_busy(src_hash, args.workload),
         "sampled_parity": ok,
         "cpu_baseline": cpu,
