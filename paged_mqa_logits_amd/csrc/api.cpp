@@ -448,9 +448,12 @@ pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const
   st = logits_common(variant, q, q_scale, kv, weights, ctx, bt, sched, workspace, s, num_heads,
                      head_dim, page_size, stream, /*fill=*/false);
   if (st != PMQA_OK) return st;
-  const hipError_t e = pmqa::launch_select_topk(workspace, s.ldo, s.batch * s.next_n, s.max_ctx,
-                                                nullptr, ctx, sched, s.batch, s.next_n,
-                                                s.workers, k, idx, val, ldk, stream);
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != PMQA_OK) return st;
+  const hipError_t e = pmqa::launch_select_topk(
+      workspace, s.ldo, s.batch * s.next_n, s.max_ctx, nullptr, ctx, sched, s.batch, s.next_n,
+      s.workers, k, idx, val, ldk, g_cus[dev].load(std::memory_order_acquire), stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -475,11 +478,13 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
                 (long long)logits_stride);
   pmqa_status_t st = check_topk_out(k, topk_indices, topk_values, topk_stride);
   if (st != PMQA_OK) return st;
-  st = check_device(nullptr);
+  int dev = 0;
+  st = check_device(&dev);
   if (st != PMQA_OK) return st;
-  const hipError_t e = pmqa::launch_select_topk(logits, logits_stride, rows, max_context_len,
-                                                lengths, nullptr, nullptr, 0, 1, 0, k,
-                                                topk_indices, topk_values, topk_stride, stream);
+  const hipError_t e = pmqa::launch_select_topk(
+      logits, logits_stride, rows, max_context_len, lengths, nullptr, nullptr, 0, 1, 0, k,
+      topk_indices, topk_values, topk_stride, g_cus[dev].load(std::memory_order_acquire),
+      stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
   return ok();
 }

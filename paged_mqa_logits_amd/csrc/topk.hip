@@ -9,7 +9,7 @@
 // ascending order with their values; a row with n < k writes all n and pads
 // with column -1, value -inf.
 //
-// One workgroup of 512 threads per row; wavefront w owns the contiguous
+// One workgroup of 512 or 1024 threads per row; wavefront w owns the contiguous
 // chunk [w*L, (w+1)*L) of the row's columns in every pass, 4 columns per
 // lane per 16-byte read.  Values are mapped to order-preserving 32-bit keys.
 //   1. One read of the row (copied into LDS when it has at most 7680
@@ -45,8 +45,7 @@ namespace pmqa {
 
 namespace {
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxSelWaves = 16;         // workgroups of 512 or 1024 threads
 constexpr int kLoads = 8;                // 16-byte reads in flight per lane
 constexpr int kTopBits = 11;             // first digit: key bits [21, 32)
 constexpr int kTopShift = 32 - kTopBits;
@@ -55,6 +54,9 @@ constexpr int kCand = 1024;              // gathered keys of the chosen bin of a
 constexpr int kStage = 7680;             // rows up to this long are kept in LDS
 constexpr int kCandLong = kStage / 2;    // ... of a longer row (in the unused stage)
 constexpr int kBins2 = 256;              // later digits: at most 8 bits
+constexpr int kWin = 4;                  // first-digit bins given a second digit in pass 1
+constexpr int kSampleRun = 256;          // a row not in LDS is sampled: the first 256
+constexpr int kSampleStride = 4096;      // columns of every 4096
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -120,8 +122,8 @@ struct SelLds {
       int32_t col[kCandLong];
     } cand_long;
   };
-  uint32_t wave_gt[kSelWaves], wave_eq[kSelWaves], wave_sum[kSelWaves];
-  uint32_t cand_cnt[kSelWaves];  // candidates each wavefront gathered
+  uint32_t wave_gt[kMaxSelWaves], wave_eq[kMaxSelWaves], wave_sum[kMaxSelWaves];
+  uint32_t cand_cnt[kMaxSelWaves];  // candidates each wavefront gathered
   uint32_t chosen[3];  // bin, keys above it, keys in it
   uint32_t ncand;
 };
@@ -163,6 +165,7 @@ __device__ __forceinline__ void for_each_tile(const float* row, const SelLds& ld
 
 // Chooses the bin of hist[0..nbins) holding the krem-th largest key (bins
 // counted from the top); every thread calls it.  Result in lds.chosen.
+template <int kSelThreads>
 __device__ __forceinline__ void choose_bin(SelLds& lds, const uint32_t* hist, int nbins,
                                            uint32_t krem) {
   const int per = (nbins + kSelThreads - 1) / kSelThreads;
@@ -201,10 +204,12 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 
 // The row of rank `rank` in decreasing count class (ties: lower row first);
 // rows <= kOrderRows.  Every thread calls it; LDS is free on return.
+template <int kSelThreads>
 __device__ __forceinline__ int32_t row_of_rank(SelLds& lds, int32_t rank, int32_t rows,
                                             int32_t max_ctx, const int32_t* lengths,
                                             const int32_t* ctx, const int32_t* sched,
                                             int32_t batch, int32_t next_n, int32_t workers) {
+  constexpr int kSelWaves = kSelThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint8_t* cls = reinterpret_cast<uint8_t*>(lds.stage);  // class of each row
   uint32_t* hist = lds.hist;
@@ -262,18 +267,20 @@ __device__ __forceinline__ int32_t row_of_rank(SelLds& lds, int32_t rank, int32_
   return r;
 }
 
+template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t max_ctx,
                         const int32_t* __restrict__ lengths, const int32_t* __restrict__ ctx,
                         const int32_t* __restrict__ sched, int32_t batch, int32_t next_n,
                         int32_t workers, int32_t k, int32_t* __restrict__ out_idx,
                         float* __restrict__ out_val, int64_t ldk) {
+  constexpr int kSelWaves = kSelThreads / 64;
   __shared__ SelLds lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t rows = (int32_t)gridDim.x;
   const int64_t r = rows <= kOrderRows
-                        ? row_of_rank(lds, (int32_t)blockIdx.x, rows, max_ctx, lengths, ctx,
+                        ? row_of_rank<kSelThreads>(lds, (int32_t)blockIdx.x, rows, max_ctx, lengths, ctx,
                                       sched, batch, next_n, workers)
                         : (int64_t)blockIdx.x;
   const float* row = logits + r * ldo;
@@ -295,10 +302,75 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
   const int32_t c0 = min(n, wave * L), c1 = min(n, c0 + L);
   const bool staged = n <= kStage;
 
-  // 1. Histogram of the top digit (and the LDS copy of a short row).
+  // Resolves the key bits under `top` of the k-th largest key among the
+  // gathered keys matching prefix under pmask (krem-th of those); digits of
+  // 8 bits, every thread calls it.
+  auto resolve = [&](uint32_t* ckey, uint32_t R, int top, uint32_t& pmask, uint32_t& prefix,
+                     uint32_t& krem) {
+    while (top > 0) {
+      const int shift = max(top - 8, 0);
+      const uint32_t dmask = (1u << (top - shift)) - 1u;
+      if (tid < kBins2) lds.hist2[tid] = 0;
+      __syncthreads();
+      for (uint32_t c = tid; c < R * kSelWaves; c += kSelThreads) {
+        const uint32_t key = ckey[c];
+        if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
+          atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      choose_bin<kSelThreads>(lds, lds.hist2, (int)dmask + 1, krem);
+      prefix |= lds.chosen[0] << shift;
+      pmask |= dmask << shift;
+      krem -= lds.chosen[1];
+      __syncthreads();
+      top = shift;
+    }
+  };
+
+  // 0. A row not kept in LDS is sampled first (256 contiguous columns of
+  //    every 4096, so every read is a whole 1 KB line run): the first-digit
+  //    bins that hold the k-th largest key with high probability (its rank
+  //    in the sample +- 4 standard deviations, at most kWin bins) get a
+  //    histogram of the second digit during pass 1.  A sample that misses
+  //    only costs the faster path below.
+  uint32_t wlo = 1, whi = 0;  // the window [wlo, whi], empty
+  uint32_t* fine = reinterpret_cast<uint32_t*>(lds.stage);  // [kWin][kBins2]
   for (int j = tid; j < kBins; j += kSelThreads) lds.hist[j] = 0;
+  if (!staged)
+    for (int j = tid; j < kWin * kBins2; j += kSelThreads) fine[j] = 0;
   if (tid == 0) lds.chosen[0] = lds.chosen[1] = lds.chosen[2] = 0;
   __syncthreads();
+  if (!staged) {
+    constexpr int32_t kRunQuads = kSampleRun / 4;
+    const int32_t groups = (n + kSampleStride - 1) / kSampleStride;
+    for (int32_t t = tid; t < groups * kRunQuads; t += kSelThreads) {
+      const int32_t col = kSampleStride * (t / kRunQuads) + 4 * (t % kRunQuads);
+      if (col < n) {
+        const v4f v = load_cols(row, lds, false, col, n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+      }
+    }
+    __syncthreads();
+    const int32_t ns = kSampleRun * (n / kSampleStride) + min(kSampleRun, n % kSampleStride);
+    const float ks = (float)k * (float)ns / (float)n;
+    const float m = 4.f * sqrtf(ks) + 4.f;
+    const uint32_t r_hi = (uint32_t)max(1.f, floorf(ks - m));
+    const uint32_t r_lo = (uint32_t)min((float)ns, ceilf(ks + m));
+    choose_bin<kSelThreads>(lds, lds.hist, kBins, r_hi);
+    whi = lds.chosen[0];
+    __syncthreads();
+    choose_bin<kSelThreads>(lds, lds.hist, kBins, r_lo);
+    wlo = max(lds.chosen[0], whi >= kWin - 1 ? whi - (kWin - 1) : 0u);
+    __syncthreads();
+    for (int j = tid; j < kBins; j += kSelThreads) lds.hist[j] = 0;
+    if (tid == 0) lds.chosen[0] = lds.chosen[1] = lds.chosen[2] = 0;
+    __syncthreads();
+  }
+
+  // 1. Histogram of the top digit (and the LDS copy of a short row, or the
+  //    second-digit histograms of the window).
   for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
     if (staged && i < c1) {
       if (i + 4 <= c1) {
@@ -309,15 +381,104 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i + e < c1) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+    for (int e = 0; e < 4; ++e) {
+      if (i + e < c1) {
+        const uint32_t key = order_key(v[e]);
+        const uint32_t bin = key >> kTopShift;
+        atomicAdd(&lds.hist[bin], 1u);
+        if (bin >= wlo && bin <= whi)
+          atomicAdd(&fine[(bin - wlo) * kBins2 + ((key >> (kTopShift - 8)) & 0xFFu)], 1u);
+      }
+    }
   });
   __syncthreads();
-  choose_bin(lds, lds.hist, kBins, (uint32_t)k);
+  choose_bin<kSelThreads>(lds, lds.hist, kBins, (uint32_t)k);
   const uint32_t b1 = lds.chosen[0];
   uint32_t krem = (uint32_t)k - lds.chosen[1];
   const uint32_t h1 = lds.chosen[2];
   __syncthreads();
+
+  // 1b. The window held the k-th largest key: its top 19 bits are known
+  //     now, and one more pass gathers every key at or above them (at most
+  //     k - 1 above plus the few sharing them) in column order; the k-th key
+  //     and the ordered write then work on that list alone.
+  if (b1 >= wlo && b1 <= whi && h1 != krem) {
+    choose_bin<kSelThreads>(lds, fine + (b1 - wlo) * kBins2, kBins2, krem);
+    const uint32_t b2 = lds.chosen[0];
+    uint32_t krem2 = krem - lds.chosen[1];
+    __syncthreads();  // the gather below overwrites the window histograms
+    constexpr int kShift2 = kTopShift - 8;
+    uint32_t pmask2 = ~0u << kShift2, prefix2 = ((b1 << 8) | b2) << kShift2;
+    const uint32_t R = (uint32_t)kCandLong / kSelWaves;
+    uint32_t* ckey = lds.cand_long.key;
+    int32_t* ccol = lds.cand_long.col;
+    uint32_t mine = 0;
+    for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
+      uint64_t bc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bc[e] = __ballot(i + e < c1 && order_key(v[e]) >= prefix2);
+      uint32_t slot = mine;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (((bc[e] >> lane) & 1u) && slot < R) {
+          ckey[wave * R + slot] = order_key(v[e]);
+          ccol[wave * R + slot] = i + e;
+        }
+        slot += (bc[e] >> lane) & 1u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
+    });
+    if (lane == 0) lds.cand_cnt[wave] = mine;
+    __syncthreads();
+    bool overflow = false;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) overflow = overflow || lds.cand_cnt[w] > R;
+    if (!overflow) {
+      resolve(ckey, R, kShift2, pmask2, prefix2, krem2);
+      // prefix2 is the k-th largest key K; krem2 keys equal to it are taken
+      const uint32_t cnt = lds.cand_cnt[wave];
+      uint32_t g = 0, q = 0;
+      for (uint32_t c = lane; c < cnt; c += 64) {
+        const uint32_t key = ckey[wave * R + c];
+        g += key > prefix2 ? 1u : 0u;
+        q += key == prefix2 ? 1u : 0u;
+      }
+      g = wave_sum(g);
+      q = wave_sum(q);
+      if (lane == 0) {
+        lds.wave_gt[wave] = g;
+        lds.wave_eq[wave] = q;
+      }
+      __syncthreads();
+      uint32_t pos = 0, eq_rank = 0;
+      for (int w = 0; w < wave; ++w) {
+        const uint32_t gw = lds.wave_gt[w], qw = lds.wave_eq[w];
+        pos += gw + (eq_rank < krem2 ? min(qw, krem2 - eq_rank) : 0u);
+        eq_rank += qw;
+      }
+      for (uint32_t c0l = 0; c0l < cnt; c0l += 64) {
+        const uint32_t c = c0l + lane;
+        const bool in = c < cnt;
+        const uint32_t key = in ? ckey[wave * R + c] : 0u;
+        const uint64_t be = __ballot(in && key == prefix2);
+        const uint32_t my_eq = eq_rank + lanes_below(be);
+        const bool sel = in && (key > prefix2 || (key == prefix2 && my_eq < krem2));
+        const uint64_t bs = __ballot(sel);
+        const uint32_t p = pos + lanes_below(bs);
+        if (sel && p < (uint32_t)k) {
+          oi[p] = ccol[wave * R + c];
+          if (ov) ov[p] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+        }
+        pos += __builtin_popcountll(bs);
+        eq_rank += __builtin_popcountll(be);
+      }
+      return;
+    }
+    __syncthreads();  // the list is abandoned; the path below reuses its space
+  }
 
   // 2. The k-th largest key K (bits under pmask, the others free) and the
   //    per-wavefront counts of keys above K and equal to K.
@@ -366,24 +527,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
     for (int w = 0; w < kSelWaves; ++w) overflow = overflow || lds.cand_cnt[w] > R;
     if (!overflow) {
       // resolve the low 21 bits on the gathered keys: digits of 8, 8, 5 bits
-      for (int top = kTopShift; top > 0;) {
-        const int shift = max(top - 8, 0);
-        const uint32_t dmask = (1u << (top - shift)) - 1u;
-        if (tid < kBins2) lds.hist2[tid] = 0;
-        __syncthreads();
-        for (uint32_t c = tid; c < R * kSelWaves; c += kSelThreads) {
-          const uint32_t key = ckey[c];
-          if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
-            atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        choose_bin(lds, lds.hist2, (int)dmask + 1, krem);
-        prefix |= lds.chosen[0] << shift;
-        pmask |= dmask << shift;
-        krem -= lds.chosen[1];
-        __syncthreads();
-        top = shift;
-      }
+      resolve(ckey, R, kTopShift, pmask, prefix, krem);
       // each wavefront counts its own candidates above K and equal to K
       uint32_t g = 0, q = 0;
       for (uint32_t c = lane; c < lds.cand_cnt[wave]; c += 64) {
@@ -417,7 +561,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
         }
       });
       __syncthreads();
-      choose_bin(lds, lds.hist2, (int)dmask + 1, krem);
+      choose_bin<kSelThreads>(lds, lds.hist2, (int)dmask + 1, krem);
       prefix |= lds.chosen[0] << shift;
       pmask |= dmask << shift;
       const uint32_t h = lds.chosen[2];
@@ -508,14 +652,24 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
 
 }  // namespace
 
+// Workgroups of 1024 threads when every row can have one at once (two per
+// compute unit), else of 512 (four per compute unit): measured on MI355X,
+// 512 rows of up to 131072 columns select in 90-110 us with 1024 threads
+// against 104-130 us with 512, and 2048 rows of up to 65536 in 64 us with
+// 512 against 84 us with 1024.
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
-                              int32_t* out_idx, float* out_val, int64_t ldk,
+                              int32_t* out_idx, float* out_val, int64_t ldk, int32_t cus,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(select_topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, logits, ldo,
-                     max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
-                     ldk);
+  if ((int64_t)rows <= 2 * (int64_t)cus)
+    hipLaunchKernelGGL(select_topk_kernel<1024>, dim3(rows), dim3(1024), 0, stream, logits, ldo,
+                       max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
+                       ldk);
+  else
+    hipLaunchKernelGGL(select_topk_kernel<512>, dim3(rows), dim3(512), 0, stream, logits, ldo,
+                       max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
+                       ldk);
   return hipGetLastError();
 }
 
