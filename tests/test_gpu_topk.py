@@ -62,6 +62,28 @@ def test_select_topk_many_rows(rows):
         assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
 
 
+def test_select_topk_long_rows_sample_misses_and_overflows():
+    """Rows too long for LDS are sampled (256 of every 4096 columns) to guess
+    the bins of the k-th key.  An unrepresentative sample (the columns it
+    reads hold only small values) and a gathered list that overflows one
+    wavefront's share (every large value in the first eighth of the row)
+    must both fall back to the exact three-pass path."""
+    announce("select_topk sample misses / overflow")
+    rng = np.random.default_rng(21)
+    rows, M, k = 4, 65536, 2048
+    x = rng.standard_normal((rows, M)).astype(np.float32)
+    sampled = (np.arange(M) % 4096) < 256
+    x[0, sampled] -= np.float32(100.0)              # the sample sees only small values
+    x[1, : M // 8] += np.float32(10.0)              # all large values in one chunk
+    n = np.array([M, M, M, 7681], np.int32)
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(rows):
+        wi, wv = otk.select_topk(x[r], int(n[r]), k)
+        assert np.array_equal(idx[r], wi), r
+        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+
+
 def test_select_topk_long_rows():
     announce("select_topk 131072 columns")
     rng = np.random.default_rng(9)
