@@ -155,10 +155,21 @@ struct Iter {
     if (b >= v.rows) return make(v.rows, 0, 0, 0);
     return make(b, u, sload(a->ctx + b), units_of(v, b));
   }
-  // First unit of the worker, from its schedule start (clamped).
+  // First unit of the worker, from its schedule start (clamped).  A start
+  // names a unit of its row, so the row's prefix sums, length and
+  // block-table entries are all requested at once (one round trip of
+  // scalar loads); the loop is for starts that do not.
   __device__ __forceinline__ Unit first(int32_t b, int32_t u) const {
     b = min(max(b, 0), v.rows);
     u = max(u, 0);
+    const int32_t bb = min(b, a->batch - 1);
+    Unit t = make(b, u, 0, 0);  // block-table entries first: nothing they need is loaded
+    const int32_t s0 = sload(v.S + bb), s1 = sload(v.S + bb + 1), len = sload(a->ctx + bb);
+    __asm__ volatile("" ::"s"(s0), "s"(s1), "s"(len), "s"(t.raw[0]), "s"(t.raw[1]),
+                     "s"(t.raw[2]), "s"(t.raw[3]));
+    t.len = len;
+    t.units = min(max(s1 - s0, 0), v.cap);
+    if (b >= v.rows || u < t.units) return t;
     while (b < v.rows && u >= units_of(v, b)) {
       ++b;
       u = 0;
@@ -545,7 +556,15 @@ void logits_kernel(const LogitsArgs a) {
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wid = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
   if (wid >= a.num_workers) return;
+  // The worker's range is requested together with the header (a buffer
+  // for this call's batch and worker count holds it, whatever the header
+  // says): one round trip.  The empty asm takes every value, so that no
+  // load is sunk below the first use of another.
+  const int32_t* range = a.sched + kSchedHeader + 2 * wid;
+  const int32_t start_b = sload(range), start_u = sload(range + 1);
+  const int32_t end_b = sload(range + 2), end_u = sload(range + 3);
   const SchedView v = make_view(a);
+  __asm__ volatile("" ::"s"(start_b), "s"(start_u), "s"(end_b), "s"(end_u), "s"(v.rows));
   if (v.rows == 0) return;
   float* stage = stage_all[wave];
   int32_t* meta = meta_all[wave];
@@ -553,18 +572,20 @@ void logits_kernel(const LogitsArgs a) {
   Iter it;
   it.v = v;
   it.a = &a;
-  it.end_b = sload(v.starts + 2 * wid + 2);
-  it.end_u = sload(v.starts + 2 * wid + 3);
-  Unit cur = it.first(sload(v.starts + 2 * wid), sload(v.starts + 2 * wid + 1));
+  it.end_b = end_b;
+  it.end_u = end_u;
+  Unit cur = it.first(start_b, start_u);
   if (!it.valid(cur)) return;
   const int32_t rows = v.rows;
+  // The first row's query block and weights are requested before the first
+  // pages, so waiting for them does not wait for the pages too.
+  RowState<Fmt, NN, HG> rs;
+  load_row<Fmt, NN, HG>(a, cur.b, lane, rs);
   // K ring: page p of a unit always lives in slot p, so the 4 pages of the
   // next unit are in flight while the current one is consumed.
   typename Fmt::KFrag ring[kPagesPerUnit];
 #pragma unroll
   for (int p = 0; p < kPagesPerUnit; ++p) load_page<Fmt>(a, cur, p, rows, lane, ring[p]);
-  RowState<Fmt, NN, HG> rs;
-  rs.b = -1;
   int32_t staged = 0;
   uint32_t phase = flush_phase(a.flush_ticks);
   // One exit, after the flush of the last unit, so the load counter has the
