@@ -17,8 +17,11 @@
 //   A operand (query): lane l holds head 16*hg + (l & 15), elements
 //     [32*(l>>4), +32) of head_dim.  Loaded once per batch row.
 //   B operand (K):     lane l holds token 16*tg + (l & 15), the same element
-//     range.  Loaded straight from HBM into VGPRs with 16-byte buffer loads:
-//     every K byte is used by exactly one lane, so no LDS staging is needed.
+//     range.  Every K byte is used by exactly one lane.  A page is read with
+//     contiguous 16-byte non-temporal loads (1 KB per instruction, which
+//     streams faster than loading in operand order) and reordered into the
+//     operand layout through a small LDS buffer of the wavefront's own (the
+//     element-format policies below).
 //   C (scores):        lane l holds heads 16*hg + 4*(l>>4) + i, i = 0..3, of
 //     token 16*tg + (l & 15).
 //
@@ -30,8 +33,8 @@
 //
 // Memory pipeline
 // ---------------
-// One worker wavefront runs per SIMD (the kernel is sized for 4 wavefronts
-// per compute unit), which leaves registers for a ring of 4 K pages: while
+// One worker wavefront runs per SIMD for fp8 (two for MXFP4, whose pages
+// are half the bytes), which leaves registers for a ring of 4 K pages: while
 // a unit's 4 pages are consumed, the next unit's 4 pages are in flight.
 // K pages are read through buffer resources.  A page with no data to score
 // (past the context, or past the block table) gets a zero-size resource, so
@@ -44,9 +47,10 @@
 // lookahead and the consumer walk the same iterator, so they always agree on
 // which (row, unit) comes next, including across skipped zero-length rows.
 //
-// Every output column is first set to -inf by a separate kernel
-// (tail_fill.hip) launched right before this one; this kernel overwrites the
-// columns of the units it processes.
+// Finished logits are staged in LDS and written in bursts, at moments
+// shared by all workers (see Stage below).  Every output column is first set
+// to -inf by a separate kernel (tail_fill.hip) launched right before this
+// one; this kernel overwrites the columns of the units it processes.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -9,24 +9,33 @@
 // ascending order with their values; a row with n < k writes all n and pads
 // with column -1, value -inf.
 //
-// One workgroup of 512 or 1024 threads per row; wavefront w owns the contiguous
-// chunk [w*L, (w+1)*L) of the row's columns in every pass, 4 columns per
-// lane per 16-byte read.  Values are mapped to order-preserving 32-bit keys.
+// One workgroup of 512 or 1024 threads per row; wavefront w owns the
+// contiguous chunk [w*L, (w+1)*L) of the row's columns in every pass, 4
+// columns per lane per 16-byte read.  Values are mapped to order-preserving
+// 32-bit keys.
 //   1. One read of the row (copied into LDS when it has at most 7680
 //      columns) builds a histogram of the keys' top 11 bits; the bin that
 //      holds the k-th largest key is b.
 //   2. A second pass gathers the keys of bin b with their columns (when
 //      there are at most 1024 of them, or 3840 for a row not copied to LDS,
 //      whose gather goes where the copy would be) and counts, per wavefront,
-//      the keys
-//      above bin b.  The remaining 21 bits of the k-th largest key K are
-//      found on the gathered list alone, which also gives each wavefront's
-//      count of keys above K and equal to K.  (A larger bin is resolved with
-//      further digit passes over the row and a counting pass instead.)
+//      the keys above bin b.  The remaining 21 bits of the k-th largest key
+//      K are found on the gathered list alone, which also gives each
+//      wavefront's count of keys above K and equal to K.  (A larger bin is
+//      resolved with further digit passes over the row and a counting pass
+//      instead.)
 //   3. A last pass writes the selected columns in order: keys above K, and
 //      the first ones (by column) equal to K; each wavefront starts at the
 //      output position the counts give it and ranks its columns with
 //      ballots.
+// A row not copied to LDS is sampled before step 1 (256 of every 4096
+// columns) to guess the bins near the k-th key; step 1 then also histograms
+// the next 8 bits of those bins, so when the guess holds, the k-th key's top
+// 19 bits are known after step 1, step 2 gathers every key at or above them
+// (the k - 1 above plus the few sharing them) in column order, and steps 2-3
+// run on that list without reading the row a third time.  A guess that
+// misses, or a list that would overflow a wavefront's share, takes the path
+// above.
 // Every pass reads 8 tiles ahead (8 16-byte reads in flight per lane for a
 // row in global memory; after the first pass they hit L2).
 //
