@@ -34,6 +34,7 @@ timed call, outside its timed interval (mall_scrub: true).
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -54,11 +55,24 @@ KERNEL_SOURCES = ["csrc/logits_kernel.hpp", "csrc/logits_fp8.hip", "csrc/tail_fi
                   "csrc/pmqa_internal.h", "csrc/api.cpp", "build.py"]
 
 
+def strip_comments(text, python=False):
+    """Source text without its comments and blank lines, so that editing a
+    comment keeps the hash (the sources here hold no comment markers inside
+    string literals)."""
+    if python:
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash():
+    """Hash of the sources that determine the timed kernels (code only)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_mqa_logits_amd", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_mqa_logits_amd", name)) as f:
+            h.update(strip_comments(f.read(), name.endswith(".py")).encode())
     return h.hexdigest()[:16]
 
 
