@@ -81,8 +81,9 @@ def algorithmic_bytes(ctx, next_n, max_ctx, heads, dim, page, sched_bytes, varia
 
     fp8: 128 E4M3 bytes + a 4-byte scale per KV token, q 128 B + weight 4 B
     per head.  fp4: 64 packed bytes + 4 E8M0 scales per KV token, q 64 B + 4
-    scales + weight 4 B per head.  K is counted once per batch row."""
-    ctx = ctx.astype(np.int64)
+    scales + weight 4 B per head.  K is counted once per batch row, up to
+    max_ctx tokens (later tokens are truncated, never read)."""
+    ctx = np.clip(ctx.astype(np.int64), 0, max_ctx)
     B = len(ctx)
     per_tok = dim + 4 if variant == "fp8" else dim // 2 + dim // 32
     per_head = dim + 4 if variant == "fp8" else dim // 2 + dim // 32 + 4
