@@ -4,9 +4,10 @@
  * The operation is the scoring step of a DeepSeek-style sparse-attention
  * indexer described on the page "[flashinfer] Blackwell 아키텍처를 위한
  * 고성능 Paged MQA Logits 커널 도입" (introduction: the indexer selects KV
- * tokens from a per-head weighted sum of rectified scores; an fp8 and an fp4
- * kernel).  For output row r (query j of batch row b, r = b*next_n + j) and
- * KV token t reached through the block table:
+ * tokens by a score that passes each head's query-key product through ReLU,
+ * weights it per head and sums; an fp8 and an fp4 kernel).  For output
+ * row r (query j of batch row b, r = b*next_n + j) and KV token t reached
+ * through the block table:
  *
  *     logits[r, t] = sum_h w[r, h] * ReLU(scale_t * dot(q[r, h, :], k_t))
  *                                        for t <  ctx_b - next_n + 1 + j
@@ -166,7 +167,7 @@ pmqa_status_t refresh_schedule(const int32_t* context_lens, int32_t batch, int32
 /*
  * paged_mqa_logits_fp8 - logits from an fp8 paged K cache.
  *
- * Page: introduction (fp8 kernel, weighted sum of rectified scores) and
+ * Page: introduction (fp8 kernel, head scores through ReLU, weighted, summed) and
  * section 1 (zero-length rows skipped by the task iterator; an epilogue
  * sized by num_heads).
  *

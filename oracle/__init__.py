@@ -7,8 +7,8 @@ benchmark use it.
 
 What it computes is the scoring step of a sparse-attention indexer described
 on the page "[flashinfer] Blackwell 아키텍처를 위한 고성능 Paged MQA Logits 커널
-도입" (introduction: a per-head weighted sum of rectified scores over paged
-KV tokens), with the formula
+도입" (introduction: ReLU of each head's score against a paged KV token,
+weighted per head and summed over heads), with the formula
 
     logits[r, t] = sum_h w[r, h] * ReLU(scale_t * q[r, h, :] . k_t)
 

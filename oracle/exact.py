@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 This is a second, deliberately different way of computing the definition in
 ``oracle/reference.py`` (page "[flashinfer] ... Paged MQA Logits ...",
-introduction: per-head weighted sum of rectified scores), used to pin that
+introduction: head scores passed through ReLU, weighted and summed), used to pin that
 module.  It shares none of its code:
 
 * element decoding goes through torch's ``float8_e4m3fn`` / ``float8_e8m0fnu``

@@ -5,10 +5,11 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 Definition followed
 -------------------
 Page "[flashinfer] Blackwell 아키텍처를 위한 고성능 Paged MQA Logits 커널 도입",
-introduction: the sparse-attention indexer picks KV tokens using a per-head
-weighted sum of rectified scores, computed by an fp8 and an fp4 kernel over a
-paged KV cache.  Written out (the plain reading of "weighted sum of rectified
-scores" with a per-token K scale):
+introduction: the sparse-attention indexer chooses KV tokens by a score that
+passes each head's query-key product through ReLU, weights it per head and
+sums over heads; an fp8 and an fp4 kernel compute it over a paged KV cache.
+Written out (the plain reading of that description, with a per-token K
+scale):
 
     S[r, h, t]  = sum_d q[r, h, d] * k[t, d]                 (exact in fp64)
     X[r, h, t]  = scale_t * S[r, h, t]

@@ -2,8 +2,8 @@
 // element formats.
 //
 // Page "[flashinfer] Blackwell 아키텍처를 위한 고성능 Paged MQA Logits 커널 도입":
-// introduction (per-head weighted sum of rectified scores, fp8 and fp4
-// kernels), section 1 (the task iterator skips zero-length rows) and the
+// introduction (the indexer score: ReLU of each head's score, weighted
+// per head and summed; fp8 and fp4 kernels), section 1 (the task iterator skips zero-length rows) and the
 // general lessons (lookahead and the task iterator must pick the same rows).
 //
 // Mapping onto CDNA4
