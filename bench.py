@@ -380,16 +380,20 @@ def main():
     ws = torch.empty_like(out)
     tk_idx = torch.empty((B * NN, K_TOP), dtype=torch.int32, device="cuda")
     tk_val = torch.empty((B * NN, K_TOP), dtype=torch.float32, device="cuda")
+    sel_bytes = pmqa.select_workspace_bytes(B * NN)
+    sel_ws = torch.empty(sel_bytes, dtype=torch.uint8, device="cuda") if sel_bytes else None
 
     def topk_call():
         if fp8:
             pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
                                     dev["context_lens"], dev["block_table"], sched, M, K_TOP,
-                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W)
+                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
+                                    select_workspace=sel_ws)
         else:
             pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
                                     dev["context_lens"], dev["block_table"], sched, M, K_TOP,
-                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W)
+                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
+                                    select_workspace=sel_ws)
 
     pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
     lengths = torch.from_numpy(np.clip(ctx_np.astype(np.int64).repeat(NN) - NN + 1 +
@@ -397,8 +401,12 @@ def main():
     topk = {"k": K_TOP,
             "fused_call_us": round(per_call_us(topk_call, args.steps), 2),
             "select_only_us": round(per_call_us(
-                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val),
-                args.steps), 2)}
+                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
+                                         select_workspace=sel_ws), args.steps), 2),
+            "select_single_kernel_us": round(per_call_us(
+                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
+                                         select_workspace=None), args.steps), 2),
+            "select_workspace_mb": round(sel_bytes / 2**20, 1)}
 
     # decode drift: every non-empty row grows by one token per step, so rows
     # cross 256-token boundaries as decoding goes on; the graph refreshes the

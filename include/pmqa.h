@@ -247,13 +247,33 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
  *                   [0, k) written.
  *   topk_values     fp32 [rows, topk_stride] or NULL.
  *   topk_stride     >= k.
+ *   select_workspace        NULL, or a device buffer of at least
+ *                   pmqa_select_workspace_bytes(rows) bytes, 16-byte aligned,
+ *                   owned by the caller, contents unspecified before and
+ *                   after the call (error PMQA_ERR_INVALID_ARGUMENT when
+ *                   smaller or misaligned).  With it, the rows too long to
+ *                   be kept in LDS are split into chunks over many
+ *                   workgroups (two more kernels run first); the result is
+ *                   the same.  Calls that share one workspace must be
+ *                   ordered (one stream).
+ *   select_workspace_bytes  its size.
  *
- * One workgroup per row; no host synchronization; can be graph-captured.
+ * One workgroup per row for the final selection; no host synchronization;
+ * can be graph-captured.
  */
 pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
                           int32_t max_context_len, const int32_t* lengths, int32_t k,
                           int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                          void* select_workspace, size_t select_workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * pmqa_select_workspace_bytes - bytes of the optional select_workspace of
+ * select_topk and paged_mqa_topk_fp8/fp4 for `rows` rows (about 49 KB per
+ * row); 0 when no workspace would be used (rows < 1 or rows > 8192).
+ * Host-only arithmetic.
+ */
+size_t pmqa_select_workspace_bytes(int32_t rows);
 
 /*
  * paged_mqa_topk_fp8 / paged_mqa_topk_fp4 - the indexer step: logits of
@@ -269,13 +289,14 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
  * (at least 0; 0 for every row when the schedule header does not describe
  * the call).
  *
- *   k, topk_indices, topk_values, topk_stride   as select_topk, with
- *                   batch*next_n rows.
+ *   k, topk_indices, topk_values, topk_stride, select_workspace,
+ *   select_workspace_bytes   as select_topk, with batch*next_n rows.
  */
 pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const float* weights,
                                  const int32_t* context_lens, const int32_t* block_table,
                                  const int32_t* schedule, float* logits_workspace, int32_t k,
                                  int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                                 void* select_workspace, size_t select_workspace_bytes,
                                  int32_t batch, int32_t next_n, int32_t num_heads,
                                  int32_t head_dim, int32_t page_size, int64_t num_pages,
                                  int32_t block_table_stride, int32_t max_context_len,
@@ -284,7 +305,8 @@ pmqa_status_t paged_mqa_topk_fp4(const void* q, const void* q_scale, const void*
                                  const float* weights, const int32_t* context_lens,
                                  const int32_t* block_table, const int32_t* schedule,
                                  float* logits_workspace, int32_t k, int32_t* topk_indices,
-                                 float* topk_values, int64_t topk_stride, int32_t batch,
+                                 float* topk_values, int64_t topk_stride, void* select_workspace,
+                                 size_t select_workspace_bytes, int32_t batch,
                                  int32_t next_n, int32_t num_heads, int32_t head_dim,
                                  int32_t page_size, int64_t num_pages,
                                  int32_t block_table_stride, int32_t max_context_len,

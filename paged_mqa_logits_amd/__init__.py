@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
                          block_table, schedule, max_context_len, out=None)
     select_topk(logits, lengths, k) -> (indices, values)
+    select_workspace_bytes(rows)
     paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table,
                        schedule, max_context_len, k) -> (indices, values)
     paged_mqa_topk_fp4(q, q_scale, kv_cache, ..., k) -> (indices, values)
@@ -51,7 +52,8 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED
 EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
            "compute_schedule", "compute_schedule_linear", "refresh_schedule",
            "paged_mqa_logits_fp8", "paged_mqa_logits_fp4", "quantize_append_fp8",
-           "quantize_append_fp4", "select_topk", "paged_mqa_topk_fp8", "paged_mqa_topk_fp4")
+           "quantize_append_fp4", "select_topk", "paged_mqa_topk_fp8", "paged_mqa_topk_fp4",
+           "pmqa_select_workspace_bytes")
 
 
 class PmqaError(RuntimeError):
@@ -68,7 +70,7 @@ if not os.path.exists(LIB_PATH):
                       "`python paged_mqa_logits_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
-_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_i32, _i64, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
 _lib.pmqa_last_error.restype = ctypes.c_char_p
 _lib.pmqa_last_error.argtypes = []
@@ -86,13 +88,17 @@ _lib.paged_mqa_logits_fp8.restype = ctypes.c_int
 _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                       _i64, _i32, _i32, _i64, _i32, _p]
 _lib.select_topk.restype = ctypes.c_int
-_lib.select_topk.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p]
+_lib.select_topk.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p, _sz, _p]
+_lib.pmqa_select_workspace_bytes.restype = _sz
+_lib.pmqa_select_workspace_bytes.argtypes = [_i32]
 _lib.paged_mqa_topk_fp8.restype = ctypes.c_int
-_lib.paged_mqa_topk_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _i32, _i32,
-                                    _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32, _p]
+_lib.paged_mqa_topk_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _p, _sz,
+                                    _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32,
+                                    _p]
 _lib.paged_mqa_topk_fp4.restype = ctypes.c_int
-_lib.paged_mqa_topk_fp4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _i32,
-                                    _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32, _p]
+_lib.paged_mqa_topk_fp4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _p, _sz,
+                                    _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32,
+                                    _p]
 _lib.quantize_append_fp8.restype = ctypes.c_int
 _lib.quantize_append_fp8.argtypes = [_p, _i32, _i64, _i32, _p, _p, _i64, _p]
 _lib.quantize_append_fp4.restype = ctypes.c_int
@@ -297,9 +303,33 @@ def _topk_out(indices, values, rows, k, want_values, device):
     return indices, values, indices.stride(0)
 
 
-def select_topk(logits, lengths, k, indices=None, values=None, want_values=True, stream=None):
+def select_workspace_bytes(rows):
+    """Bytes of the optional top-k split workspace for `rows` rows (0: none used)."""
+    return int(_lib.pmqa_select_workspace_bytes(int(rows)))
+
+
+def _select_ws(select_workspace, rows, device):
+    """(pointer, bytes) of the top-k split workspace: "auto" allocates one,
+    None passes none, a uint8 tensor is used as given."""
+    if select_workspace is None:
+        return None, 0
+    if isinstance(select_workspace, str):
+        if select_workspace != "auto":
+            raise ValueError('select_workspace must be "auto", None or a tensor')
+        n = select_workspace_bytes(rows)
+        if n == 0:
+            return None, 0
+        select_workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    _need(select_workspace, "select_workspace", (torch.uint8,), ndim=1)
+    return select_workspace, select_workspace.numel()
+
+
+def select_topk(logits, lengths, k, indices=None, values=None, want_values=True,
+                select_workspace="auto", stream=None):
     """Top k of each row's first lengths[r] columns, ascending column order;
-    returns (indices int32 [rows, k], values fp32 [rows, k] or None)."""
+    returns (indices int32 [rows, k], values fp32 [rows, k] or None).
+    select_workspace: "auto" (allocated here), None (single-kernel path) or a
+    uint8 tensor of at least select_workspace_bytes(rows) bytes."""
     _need(logits, "logits", (torch.float32,), ndim=2, contiguous=False)
     _need(lengths, "lengths", (torch.int32,), ndim=1)
     rows, M = logits.shape
@@ -308,23 +338,29 @@ def select_topk(logits, lengths, k, indices=None, values=None, want_values=True,
     if lengths.shape[0] != rows:
         raise ValueError("lengths must have one entry per row")
     indices, values, ldk = _topk_out(indices, values, rows, int(k), want_values, logits.device)
+    ws, ws_bytes = _select_ws(select_workspace, rows, logits.device)
     _check(_lib.select_topk(_ptr(logits), logits.stride(0), rows, M, _ptr(lengths), int(k),
-                            _ptr(indices), _ptr(values), ldk, _stream_ptr(stream)))
+                            _ptr(indices), _ptr(values), ldk, _ptr(ws), ws_bytes,
+                            _stream_ptr(stream)))
     return indices[:, :k], None if values is None else values[:, :k]
 
 
 def paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table, schedule,
                        max_context_len, k, workspace=None, indices=None, values=None,
-                       want_values=True, num_workers=None, stream=None):
+                       want_values=True, num_workers=None, select_workspace="auto",
+                       stream=None):
     """The fp8 indexer step: logits of every scheduled unit into `workspace`
-    (no -inf fill), then the top k per output row; returns (indices, values)."""
+    (no -inf fill), then the top k per output row; returns (indices, values).
+    select_workspace as in select_topk."""
     B, NN, H, D = _fp8_shapes(q, kv_cache, weights, context_lens, block_table, schedule)
     W = _sched_workers(schedule, B, num_workers)
     _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
     indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
+    ws, ws_bytes = _select_ws(select_workspace, B * NN, q.device)
     _check(_lib.paged_mqa_topk_fp8(
         _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
-        _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk, B, NN, H, D,
+        _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk, _ptr(ws), ws_bytes,
+        B, NN, H, D,
         PAGE_SIZE, kv_cache.shape[0], block_table.shape[1], int(max_context_len), ldo, W,
         _stream_ptr(stream)))
     return indices[:, :k], None if values is None else values[:, :k]
@@ -332,16 +368,18 @@ def paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table, schedule
 
 def paged_mqa_topk_fp4(q, q_scale, kv_cache, weights, context_lens, block_table, schedule,
                        max_context_len, k, workspace=None, indices=None, values=None,
-                       want_values=True, num_workers=None, stream=None):
+                       want_values=True, num_workers=None, select_workspace="auto",
+                       stream=None):
     """The MXFP4 indexer step (see paged_mqa_topk_fp8)."""
     B, NN, H, D = _fp4_shapes(q, q_scale, kv_cache, weights, context_lens, block_table, schedule)
     W = _sched_workers(schedule, B, num_workers)
     _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
     indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
+    ws, ws_bytes = _select_ws(select_workspace, B * NN, q.device)
     _check(_lib.paged_mqa_topk_fp4(
         _ptr(q), _ptr(q_scale), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
         _ptr(block_table), _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk,
-        B, NN, H, D, PAGE_SIZE, kv_cache.shape[0], block_table.shape[1],
+        _ptr(ws), ws_bytes, B, NN, H, D, PAGE_SIZE, kv_cache.shape[0], block_table.shape[1],
         int(max_context_len), ldo, W, _stream_ptr(stream)))
     return indices[:, :k], None if values is None else values[:, :k]
 

@@ -427,7 +427,8 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
 
 namespace {
 
-pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, int64_t ldk) {
+pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, int64_t ldk,
+                             int32_t rows, const void* ws, size_t ws_bytes) {
   if (k < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "k = %d must be >= 1", k);
   if (!idx) return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_indices is null");
   if (!aligned(idx, 4) || (val && !aligned(val, 4)))
@@ -435,15 +436,25 @@ pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, in
   if (ldk < k)
     return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_stride = %lld must be >= k = %d",
                 (long long)ldk, k);
+  if (ws) {
+    if (!aligned(ws, 16))
+      return fail(PMQA_ERR_INVALID_ARGUMENT, "select_workspace must be 16-byte aligned");
+    const size_t need = pmqa::select_workspace_bytes(rows);
+    if (ws_bytes < need)
+      return fail(PMQA_ERR_INVALID_ARGUMENT,
+                  "select_workspace_bytes = %zu < %zu needed for %d rows", ws_bytes, need, rows);
+  }
   return PMQA_OK;
 }
 
 pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const void* kv,
                           const float* weights, const int32_t* ctx, const int32_t* bt,
                           const int32_t* sched, float* workspace, int32_t k, int32_t* idx,
-                          float* val, int64_t ldk, const Shape& s, int32_t num_heads,
-                          int32_t head_dim, int32_t page_size, hipStream_t stream) {
-  pmqa_status_t st = check_topk_out(k, idx, val, ldk);
+                          float* val, int64_t ldk, void* sel_ws, size_t sel_ws_bytes,
+                          const Shape& s, int32_t num_heads, int32_t head_dim, int32_t page_size,
+                          hipStream_t stream) {
+  const int32_t rows = (int32_t)std::min<int64_t>((int64_t)s.batch * s.next_n, INT32_MAX);
+  pmqa_status_t st = check_topk_out(k, idx, val, ldk, rows, sel_ws, sel_ws_bytes);
   if (st != PMQA_OK) return st;
   st = logits_common(variant, q, q_scale, kv, weights, ctx, bt, sched, workspace, s, num_heads,
                      head_dim, page_size, stream, /*fill=*/false);
@@ -453,16 +464,19 @@ pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const
   if (st != PMQA_OK) return st;
   const hipError_t e = pmqa::launch_select_topk(
       workspace, s.ldo, s.batch * s.next_n, s.max_ctx, nullptr, ctx, sched, s.batch, s.next_n,
-      s.workers, k, idx, val, ldk, g_cus[dev].load(std::memory_order_acquire), stream);
+      s.workers, k, idx, val, ldk, sel_ws, g_cus[dev].load(std::memory_order_acquire), stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
   return ok();
 }
 
 }  // namespace
 
+size_t pmqa_select_workspace_bytes(int32_t rows) { return pmqa::select_workspace_bytes(rows); }
+
 pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
                           int32_t max_context_len, const int32_t* lengths, int32_t k,
                           int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                          void* select_workspace, size_t select_workspace_bytes,
                           hipStream_t stream) {
   if (!logits) return fail(PMQA_ERR_INVALID_ARGUMENT, "logits is null");
   if (!lengths) return fail(PMQA_ERR_INVALID_ARGUMENT, "lengths is null");
@@ -476,15 +490,16 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
     return fail(PMQA_ERR_INVALID_ARGUMENT,
                 "logits_stride = %lld must be >= max_context_len and a multiple of 4",
                 (long long)logits_stride);
-  pmqa_status_t st = check_topk_out(k, topk_indices, topk_values, topk_stride);
+  pmqa_status_t st = check_topk_out(k, topk_indices, topk_values, topk_stride, rows,
+                                    select_workspace, select_workspace_bytes);
   if (st != PMQA_OK) return st;
   int dev = 0;
   st = check_device(&dev);
   if (st != PMQA_OK) return st;
   const hipError_t e = pmqa::launch_select_topk(
       logits, logits_stride, rows, max_context_len, lengths, nullptr, nullptr, 0, 1, 0, k,
-      topk_indices, topk_values, topk_stride, g_cus[dev].load(std::memory_order_acquire),
-      stream);
+      topk_indices, topk_values, topk_stride, select_workspace,
+      g_cus[dev].load(std::memory_order_acquire), stream);
   if (e != hipSuccess) return fail(PMQA_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -493,6 +508,7 @@ pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const floa
                                  const int32_t* context_lens, const int32_t* block_table,
                                  const int32_t* schedule, float* logits_workspace, int32_t k,
                                  int32_t* topk_indices, float* topk_values, int64_t topk_stride,
+                                 void* select_workspace, size_t select_workspace_bytes,
                                  int32_t batch, int32_t next_n, int32_t num_heads,
                                  int32_t head_dim, int32_t page_size, int64_t num_pages,
                                  int32_t block_table_stride, int32_t max_context_len,
@@ -500,24 +516,27 @@ pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const floa
   const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
                 logits_stride};
   return topk_common(PMQA_VARIANT_FP8, q, nullptr, kv_cache, weights, context_lens, block_table,
-                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride, s,
-                     num_heads, head_dim, page_size, stream);
+                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride,
+                     select_workspace, select_workspace_bytes, s, num_heads, head_dim, page_size,
+                     stream);
 }
 
 pmqa_status_t paged_mqa_topk_fp4(const void* q, const void* q_scale, const void* kv_cache,
                                  const float* weights, const int32_t* context_lens,
                                  const int32_t* block_table, const int32_t* schedule,
                                  float* logits_workspace, int32_t k, int32_t* topk_indices,
-                                 float* topk_values, int64_t topk_stride, int32_t batch,
-                                 int32_t next_n, int32_t num_heads, int32_t head_dim,
-                                 int32_t page_size, int64_t num_pages,
-                                 int32_t block_table_stride, int32_t max_context_len,
-                                 int64_t logits_stride, int32_t num_workers, hipStream_t stream) {
+                                 float* topk_values, int64_t topk_stride, void* select_workspace,
+                                 size_t select_workspace_bytes, int32_t batch, int32_t next_n,
+                                 int32_t num_heads, int32_t head_dim, int32_t page_size,
+                                 int64_t num_pages, int32_t block_table_stride,
+                                 int32_t max_context_len, int64_t logits_stride,
+                                 int32_t num_workers, hipStream_t stream) {
   const Shape s{batch, next_n, block_table_stride, max_context_len, num_workers, num_pages,
                 logits_stride};
   return topk_common(PMQA_VARIANT_FP4, q, q_scale, kv_cache, weights, context_lens, block_table,
-                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride, s,
-                     num_heads, head_dim, page_size, stream);
+                     schedule, logits_workspace, k, topk_indices, topk_values, topk_stride,
+                     select_workspace, select_workspace_bytes, s, num_heads, head_dim, page_size,
+                     stream);
 }
 
 }  // extern "C"

@@ -2,6 +2,7 @@
 // HIP translation units that own the kernels.  Not part of the public ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -68,12 +69,17 @@ hipError_t launch_append(int variant, const void* k, int32_t dtype, int64_t n,
 // Top-k per row of logits [rows, ldo]: candidates are the first
 // lengths[r] columns (lengths given), else the fused indexer rule from
 // ctx / sched (batch, next_n, workers).  Writes out_idx [rows, ldk] and,
-// when not null, out_val [rows, ldk].  cus: compute units of the device.
+// when not null, out_val [rows, ldk].  workspace: null, or at least
+// select_workspace_bytes(rows) bytes, 16-byte aligned (unused for more than
+// kSplitRows rows); with it, long rows are split over several workgroups.
+// cus: compute units of the device.
+constexpr int32_t kSplitRows = 8192;
+size_t select_workspace_bytes(int32_t rows);
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
-                              int32_t* out_idx, float* out_val, int64_t ldk, int32_t cus,
-                              hipStream_t stream);
+                              int32_t* out_idx, float* out_val, int64_t ldk, void* workspace,
+                              int32_t cus, hipStream_t stream);
 
 // Resident workgroups per compute unit of a logits kernel (occupancy query).
 hipError_t logits_blocks_per_cu(int variant, int next_n, int heads, int* blocks);

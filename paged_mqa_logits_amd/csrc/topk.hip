@@ -46,7 +46,25 @@
 // then start at once instead of whenever their index comes up.  Each
 // workgroup derives its row from the counts of all rows (for up to 8192
 // rows; beyond that workgroup i takes row i).
+//
+// Split rows.  With a workspace and few rows (at most two per compute unit,
+// so one workgroup per row would leave most of the chip waiting on the
+// longest rows), two kernels run before the selection:
+//   * the plan orders the rows once for all workgroups (ws.map) and gives
+//     each row not kept in LDS a key threshold from a sample of the row,
+//     chosen so that at least k keys reach it (but for a miss of several
+//     standard deviations) and about 1.4 k are expected to;
+//   * the gather reads every such row in chunks of 16384 columns or more,
+//     one workgroup per chunk, and lists the keys at or above the
+//     threshold, in column order, with their count per chunk.
+// The selection then takes a split row's list (a few thousand keys) instead
+// of the row, resolves the k-th key on it and writes from it.  A list that
+// is not whole (a chunk with more keys than its slots) or holds fewer than k
+// keys (the sample missed) sends the row down the path above; either way the
+// result is the same.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "pmqa_internal.h"
 
@@ -61,11 +79,19 @@ constexpr int kTopShift = 32 - kTopBits;
 constexpr int kBins = 1 << kTopBits;
 constexpr int kCand = 1024;              // gathered keys of the chosen bin of a staged row
 constexpr int kStage = 7680;             // rows up to this long are kept in LDS
-constexpr int kCandLong = kStage / 2;    // ... of a longer row (in the unused stage)
+constexpr int kCandLong = kStage / 2;    // ... of a longer row (in the unused stage; twice
+                                         // that with 1024 threads)
 constexpr int kBins2 = 256;              // later digits: at most 8 bits
 constexpr int kWin = 4;                  // first-digit bins given a second digit in pass 1
 constexpr int kSampleRun = 256;          // a row not in LDS is sampled: the first 256
 constexpr int kSampleStride = 4096;      // columns of every 4096
+constexpr int kListCap = kCandLong;      // keys listed for a split row, at most
+constexpr int kMaxChunks = 16;           // chunks of a split row, at most
+constexpr int32_t kChunkMin = 16384;     // columns of a chunk, at least
+constexpr int kRowSlots = 3 * kListCap / 2 + 32 * kMaxChunks;  // list slots of a row
+constexpr uint32_t kNoSplit = 0xFFFFFFFFu;  // threshold of a row that is not split
+constexpr int kPlanRun = 256;            // the plan samples 256 of every 4096 columns
+constexpr float kListFill = 0.8f;        // expected list at most this share of kListCap
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -103,8 +129,52 @@ __device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
   return (int32_t)max((int64_t)0, min(min(lim, (int64_t)kUnit * c), (int64_t)max_ctx));
 }
 
-constexpr int kOrderRows = 8192;          // rows ordered longest first
+constexpr int kOrderRows = kSplitRows;    // rows ordered longest first
 constexpr int kOrderBins = 128;           // count classes
+
+// Columns of each chunk of a split row of n candidates: at least kChunkMin,
+// and at most kMaxChunks chunks.
+__device__ __forceinline__ int32_t chunk_cols(int32_t n) {
+  const int64_t per = ((int64_t)n + kMaxChunks * 1024 - 1) / (kMaxChunks * 1024) * 1024;
+  return (int32_t)(per > kChunkMin ? per : kChunkMin);
+}
+
+// First list slot of the chunk starting at column c of a row of n
+// candidates (j chunks before it): each chunk gets 1.5 times its share of
+// kListCap by columns, plus 32 (a chunk's count varies more, relative to its
+// mean, the fewer keys it expects); kRowSlots for the row at most.
+__device__ __forceinline__ int32_t chunk_slot(int32_t c, int32_t j, int32_t n) {
+  return (int32_t)((int64_t)(3 * kListCap / 2) * c / n) + 32 * j;
+}
+
+// The workspace of the split path, in sections of whole 256-byte blocks.
+struct SplitWs {
+  int32_t* map;    // [rows]: row taken by workgroup i of the selection
+  int32_t* len;    // [rows]: candidates of each row
+  uint32_t* thr;   // [rows]: key threshold of a split row, else kNoSplit
+  int32_t* cnt;    // [rows * kMaxChunks]: keys at or above the threshold
+  uint32_t* key;   // [rows * kRowSlots]: those keys, chunk by chunk (chunk_slot)
+  int32_t* col;    // [rows * kRowSlots]: their columns
+};
+
+int64_t ws_words(int64_t n) { return (n + 63) & ~(int64_t)63; }
+
+SplitWs split_ws(void* base, int32_t rows) {
+  int32_t* p = static_cast<int32_t*>(base);
+  SplitWs w;
+  w.map = p;
+  p += ws_words(rows);
+  w.len = p;
+  p += ws_words(rows);
+  w.thr = reinterpret_cast<uint32_t*>(p);
+  p += ws_words(rows);
+  w.cnt = p;
+  p += ws_words((int64_t)rows * kMaxChunks);
+  w.key = reinterpret_cast<uint32_t*>(p);
+  p += ws_words((int64_t)rows * kRowSlots);
+  w.col = p;
+  return w;
+}
 
 // Order-preserving coarse class of a candidate count: 0 for none, else
 // 1 + 4 floor(log2 n) + the two bits below the leading one (at most 124).
@@ -115,7 +185,8 @@ __device__ __forceinline__ uint32_t count_class(int32_t n) {
   return 1u + 4u * (uint32_t)e + (uint32_t)m;
 }
 
-struct SelLds {
+template <int kLong>
+struct SelLdsT {
   union {
     uint32_t hist[kBins];        // pass 1
     struct {                     // after it
@@ -127,15 +198,22 @@ struct SelLds {
   union {
     float stage[kStage] __attribute__((aligned(16)));
     struct {
-      uint32_t key[kCandLong];
-      int32_t col[kCandLong];
+      uint32_t key[kLong];
+      int32_t col[kLong];
     } cand_long;
   };
   uint32_t wave_gt[kMaxSelWaves], wave_eq[kMaxSelWaves], wave_sum[kMaxSelWaves];
   uint32_t cand_cnt[kMaxSelWaves];  // candidates each wavefront gathered
+  int32_t chunk_cnt[kMaxChunks], chunk_lo[kMaxChunks];  // a split row's lists
   uint32_t chosen[3];  // bin, keys above it, keys in it
-  uint32_t ncand;
 };
+
+// Workgroups of 1024 threads (two per compute unit) have LDS for twice the
+// gathered list of a long row.
+template <int kSelThreads>
+constexpr int long_cap() { return kSelThreads >= 1024 ? 2 * kCandLong : kCandLong; }
+template <int kSelThreads>
+using SelLds = SelLdsT<long_cap<kSelThreads>()>;
 
 // Columns i..i+3 of a row, from LDS or global memory (two paths, so each
 // compiles to its own load instructions), columns at or past c1 as -inf.
@@ -143,7 +221,8 @@ struct SelLds {
 // one at i clamped to the last quad holding a column below c1 (rows are
 // allocated in whole quads: their stride is a multiple of 4), and the
 // columns past c1 are masked afterwards.
-__device__ __forceinline__ v4f load_cols(const float* row, const SelLds& lds, bool staged,
+template <class Lds>
+__device__ __forceinline__ v4f load_cols(const float* row, const Lds& lds, bool staged,
                                          int32_t i, int32_t c1) {
   const float ninf = -__builtin_inff();
   const int32_t q = min(i, (c1 - 1) & ~3);
@@ -157,8 +236,8 @@ __device__ __forceinline__ v4f load_cols(const float* row, const SelLds& lds, bo
 // The chunk [c0, c1) a wavefront owns, read 256 columns (4 per lane) per
 // tile: calls f(first column of the lane's 4, values) for every tile in
 // column order, kLoads tiles read ahead.
-template <class F>
-__device__ __forceinline__ void for_each_tile(const float* row, const SelLds& lds, bool staged,
+template <class Lds, class F>
+__device__ __forceinline__ void for_each_tile(const float* row, const Lds& lds, bool staged,
                                               int32_t c0, int32_t c1, F&& f) {
   const int lane = threadIdx.x & 63;
   for (int32_t b0 = c0; b0 < c1; b0 += kLoads * 256) {
@@ -172,10 +251,29 @@ __device__ __forceinline__ void for_each_tile(const float* row, const SelLds& ld
   }
 }
 
+// The sample of a row not kept in LDS: the first kRun columns of every
+// kSampleStride (so every read is part of a run of whole 1 KB lines);
+// calls f(first column of the quad, values) for every quad of it.
+template <int kSelThreads, int kRun, class Lds, class F>
+__device__ __forceinline__ void for_each_sample(const float* row, const Lds& lds, int32_t n,
+                                                F&& f) {
+  constexpr int32_t kRunQuads = kRun / 4;
+  const int32_t groups = (n + kSampleStride - 1) / kSampleStride;
+  for (int32_t t = threadIdx.x; t < groups * kRunQuads; t += kSelThreads) {
+    const int32_t col = kSampleStride * (t / kRunQuads) + 4 * (t % kRunQuads);
+    if (col < n) f(col, load_cols(row, lds, false, col, n));
+  }
+}
+
+template <int kRun>
+__device__ __forceinline__ int32_t sample_size(int32_t n) {
+  return kRun * (n / kSampleStride) + min(kRun, n % kSampleStride);
+}
+
 // Chooses the bin of hist[0..nbins) holding the krem-th largest key (bins
 // counted from the top); every thread calls it.  Result in lds.chosen.
-template <int kSelThreads>
-__device__ __forceinline__ void choose_bin(SelLds& lds, const uint32_t* hist, int nbins,
+template <int kSelThreads, class Lds>
+__device__ __forceinline__ void choose_bin(Lds& lds, const uint32_t* hist, int nbins,
                                            uint32_t krem) {
   const int per = (nbins + kSelThreads - 1) / kSelThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -213,8 +311,8 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 
 // The row of rank `rank` in decreasing count class (ties: lower row first);
 // rows <= kOrderRows.  Every thread calls it; LDS is free on return.
-template <int kSelThreads>
-__device__ __forceinline__ int32_t row_of_rank(SelLds& lds, int32_t rank, int32_t rows,
+template <int kSelThreads, class Lds>
+__device__ __forceinline__ int32_t row_of_rank(Lds& lds, int32_t rank, int32_t rows,
                                             int32_t max_ctx, const int32_t* lengths,
                                             const int32_t* ctx, const int32_t* sched,
                                             int32_t batch, int32_t next_n, int32_t workers) {
@@ -282,21 +380,25 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
                         const int32_t* __restrict__ lengths, const int32_t* __restrict__ ctx,
                         const int32_t* __restrict__ sched, int32_t batch, int32_t next_n,
                         int32_t workers, int32_t k, int32_t* __restrict__ out_idx,
-                        float* __restrict__ out_val, int64_t ldk) {
+                        float* __restrict__ out_val, int64_t ldk, SplitWs ws) {
   constexpr int kSelWaves = kSelThreads / 64;
-  __shared__ SelLds lds;
+  __shared__ SelLds<kSelThreads> lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t rows = (int32_t)gridDim.x;
-  const int64_t r = rows <= kOrderRows
-                        ? row_of_rank<kSelThreads>(lds, (int32_t)blockIdx.x, rows, max_ctx, lengths, ctx,
-                                      sched, batch, next_n, workers)
+  // with the split workspace, the plan kernel has ordered the rows and
+  // counted their candidates
+  const int64_t r = ws.map ? (int64_t)ws.map[blockIdx.x]
+                    : rows <= kOrderRows
+                        ? row_of_rank<kSelThreads>(lds, (int32_t)blockIdx.x, rows, max_ctx,
+                                                   lengths, ctx, sched, batch, next_n, workers)
                         : (int64_t)blockIdx.x;
   const float* row = logits + r * ldo;
   int32_t* oi = out_idx + r * ldk;
   float* ov = out_val ? out_val + r * ldk : nullptr;
-  const int32_t n = row_candidates((int32_t)r, max_ctx, lengths, ctx, sched, batch, next_n,
-                                   workers);
+  const int32_t n = ws.map ? ws.len[r]
+                           : row_candidates((int32_t)r, max_ctx, lengths, ctx, sched, batch,
+                                            next_n, workers);
   const float ninf = -__builtin_inff();
 
   if (n <= k) {  // every candidate is selected
@@ -313,21 +415,25 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
 
   // Resolves the key bits under `top` of the k-th largest key among the
   // gathered keys matching prefix under pmask (krem-th of those); digits of
-  // 8 bits, every thread calls it.
+  // `bits` bits counted in hist (1 << bits bins), every thread calls it.
+  // Slots from `limit` on hold no key.
   auto resolve = [&](uint32_t* ckey, uint32_t R, int top, uint32_t& pmask, uint32_t& prefix,
-                     uint32_t& krem) {
+                     uint32_t& krem, int bits = 8, uint32_t* hist = nullptr,
+                     uint32_t limit = 0xFFFFFFFFu) {
+    if (!hist) hist = lds.hist2;
+    limit = min(limit, R * kSelWaves);
     while (top > 0) {
-      const int shift = max(top - 8, 0);
+      const int shift = max(top - bits, 0);
       const uint32_t dmask = (1u << (top - shift)) - 1u;
-      if (tid < kBins2) lds.hist2[tid] = 0;
+      for (int b = tid; b <= (int)dmask; b += kSelThreads) hist[b] = 0;
       __syncthreads();
-      for (uint32_t c = tid; c < R * kSelWaves; c += kSelThreads) {
+      for (uint32_t c = tid; c < limit; c += kSelThreads) {
         const uint32_t key = ckey[c];
         if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
-          atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
+          atomicAdd(&hist[(key >> shift) & dmask], 1u);
       }
       __syncthreads();
-      choose_bin<kSelThreads>(lds, lds.hist2, (int)dmask + 1, krem);
+      choose_bin<kSelThreads>(lds, hist, (int)dmask + 1, krem);
       prefix |= lds.chosen[0] << shift;
       pmask |= dmask << shift;
       krem -= lds.chosen[1];
@@ -335,6 +441,124 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
       top = shift;
     }
   };
+
+  // Writes the selection from gathered lists (wavefront w's keys in
+  // ckey[w*R, w*R + cand_cnt[w]), the lists together in column order): the
+  // keys above K and the first keq (by column) equal to it.
+  auto write_list = [&](const uint32_t* ckey, const int32_t* ccol, uint32_t R, uint32_t K,
+                        uint32_t keq) {
+    const uint32_t cnt = lds.cand_cnt[wave];
+    uint32_t g = 0, q = 0;
+    for (uint32_t c = lane; c < cnt; c += 64) {
+      const uint32_t key = ckey[wave * R + c];
+      g += key > K ? 1u : 0u;
+      q += key == K ? 1u : 0u;
+    }
+    g = wave_sum(g);
+    q = wave_sum(q);
+    if (lane == 0) {
+      lds.wave_gt[wave] = g;
+      lds.wave_eq[wave] = q;
+    }
+    __syncthreads();
+    uint32_t pos = 0, eq_rank = 0;
+    for (int w = 0; w < wave; ++w) {
+      const uint32_t gw = lds.wave_gt[w], qw = lds.wave_eq[w];
+      pos += gw + (eq_rank < keq ? min(qw, keq - eq_rank) : 0u);
+      eq_rank += qw;
+    }
+    for (uint32_t c0l = 0; c0l < cnt; c0l += 64) {
+      const uint32_t c = c0l + lane;
+      const bool in = c < cnt;
+      const uint32_t key = in ? ckey[wave * R + c] : 0u;
+      const uint64_t be = __ballot(in && key == K);
+      const uint32_t my_eq = eq_rank + lanes_below(be);
+      const bool sel = in && (key > K || (key == K && my_eq < keq));
+      const uint64_t bs = __ballot(sel);
+      const uint32_t p = pos + lanes_below(bs);
+      if (sel && p < (uint32_t)k) {
+        oi[p] = ccol[wave * R + c];
+        if (ov) ov[p] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+      }
+      pos += __builtin_popcountll(bs);
+      eq_rank += __builtin_popcountll(be);
+    }
+  };
+
+  // A split row whose lists are whole: the plan kernel set a threshold no
+  // larger than the k-th largest key (checked here: at least k keys reach
+  // it), and the gather kernel listed every key at or above it, chunk by
+  // chunk in column order.  The selection is made on the list alone.
+  const uint32_t thr = ws.map && !staged ? ws.thr[r] : kNoSplit;
+  if (thr != kNoSplit) {
+    const int32_t C = chunk_cols(n), nch = (n + C - 1) / C;
+    if (tid < nch) {
+      const int32_t m = ws.cnt[r * kMaxChunks + tid];
+      const int32_t lo = chunk_slot(tid * C, tid, n);
+      const int32_t size = chunk_slot(min(n, (tid + 1) * C), tid + 1, n) - lo;
+      lds.chunk_lo[tid] = lo;
+      lds.chunk_cnt[tid] = (m >= 0 && m <= size) ? m : -1;  // -1: the list overflowed
+    }
+    __syncthreads();
+    int32_t total = 0;
+    bool whole = true;
+    for (int j = 0; j < nch; ++j) {
+      const int32_t m = lds.chunk_cnt[j];
+      whole = whole && m >= 0;
+      total += max(m, 0);
+    }
+    if (whole && total >= k && total <= long_cap<kSelThreads>()) {
+      uint32_t* ckey = lds.cand_long.key;
+      int32_t* ccol = lds.cand_long.col;
+      const uint32_t R = (uint32_t)long_cap<kSelThreads>() / kSelWaves;
+      // entry i of the joined list goes to slot i: wavefront i / R's list
+      // (the reads of a round are all issued before the LDS writes)
+      constexpr int kU = (long_cap<kSelThreads>() + kSelThreads - 1) / kSelThreads;
+      uint32_t kk[kU];
+      int32_t cc[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t i = tid + u * kSelThreads;
+        if (i < total) {
+          int32_t j = 0, before = 0;
+          while (before + lds.chunk_cnt[j] <= i) before += lds.chunk_cnt[j++];
+          const int64_t g = r * kRowSlots + lds.chunk_lo[j] + (i - before);
+          kk[u] = ws.key[g];
+          cc[u] = ws.col[g];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t i = tid + u * kSelThreads;
+        if (i < total) {
+          ckey[i] = kk[u];
+          ccol[i] = cc[u];
+        }
+      }
+      // the bits above the highest one where some listed key differs from
+      // the threshold are the threshold's (the keys of a row's top few
+      // percent share their sign and most exponent bits, which would put
+      // them all in a few bins of a first digit taken from the top)
+      uint32_t diff = 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (tid + u * kSelThreads < total) diff |= kk[u] ^ thr;
+      for (int off = 1; off < 64; off <<= 1) diff |= __shfl_xor(diff, off, 64);
+      if (lane == 0) lds.wave_sum[wave] = diff;
+      if (lane == 0)
+        lds.cand_cnt[wave] = (uint32_t)min(max(total - wave * (int32_t)R, 0), (int32_t)R);
+      __syncthreads();
+      diff = 0;
+      for (int w = 0; w < kSelWaves; ++w) diff |= lds.wave_sum[w];
+      const int top = diff ? 32 - __builtin_clz(diff) : 0;
+      uint32_t pmask = top == 32 ? 0u : ~0u << top, prefix = thr & pmask, krem = (uint32_t)k;
+      __syncthreads();  // wave_sum is read before choose_bin writes it
+      resolve(ckey, R, top, pmask, prefix, krem, kTopBits, lds.hist, (uint32_t)total);
+      write_list(ckey, ccol, R, prefix, krem);
+      return;
+    }
+    __syncthreads();  // the counts above are read before the path below reuses LDS
+  }
 
   // 0. A row not kept in LDS is sampled first (256 contiguous columns of
   //    every 4096, so every read is a whole 1 KB line run): the first-digit
@@ -350,19 +574,13 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
   if (tid == 0) lds.chosen[0] = lds.chosen[1] = lds.chosen[2] = 0;
   __syncthreads();
   if (!staged) {
-    constexpr int32_t kRunQuads = kSampleRun / 4;
-    const int32_t groups = (n + kSampleStride - 1) / kSampleStride;
-    for (int32_t t = tid; t < groups * kRunQuads; t += kSelThreads) {
-      const int32_t col = kSampleStride * (t / kRunQuads) + 4 * (t % kRunQuads);
-      if (col < n) {
-        const v4f v = load_cols(row, lds, false, col, n);
+    for_each_sample<kSelThreads, kSampleRun>(row, lds, n, [&](int32_t col, const v4f& v) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
-      }
-    }
+      for (int e = 0; e < 4; ++e)
+        if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+    });
     __syncthreads();
-    const int32_t ns = kSampleRun * (n / kSampleStride) + min(kSampleRun, n % kSampleStride);
+    const int32_t ns = sample_size<kSampleRun>(n);
     const float ks = (float)k * (float)ns / (float)n;
     const float m = 4.f * sqrtf(ks) + 4.f;
     const uint32_t r_hi = (uint32_t)max(1.f, floorf(ks - m));
@@ -418,7 +636,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
     __syncthreads();  // the gather below overwrites the window histograms
     constexpr int kShift2 = kTopShift - 8;
     uint32_t pmask2 = ~0u << kShift2, prefix2 = ((b1 << 8) | b2) << kShift2;
-    const uint32_t R = (uint32_t)kCandLong / kSelWaves;
+    const uint32_t R = (uint32_t)long_cap<kSelThreads>() / kSelWaves;
     uint32_t* ckey = lds.cand_long.key;
     int32_t* ccol = lds.cand_long.col;
     uint32_t mine = 0;
@@ -448,42 +666,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
     if (!overflow) {
       resolve(ckey, R, kShift2, pmask2, prefix2, krem2);
       // prefix2 is the k-th largest key K; krem2 keys equal to it are taken
-      const uint32_t cnt = lds.cand_cnt[wave];
-      uint32_t g = 0, q = 0;
-      for (uint32_t c = lane; c < cnt; c += 64) {
-        const uint32_t key = ckey[wave * R + c];
-        g += key > prefix2 ? 1u : 0u;
-        q += key == prefix2 ? 1u : 0u;
-      }
-      g = wave_sum(g);
-      q = wave_sum(q);
-      if (lane == 0) {
-        lds.wave_gt[wave] = g;
-        lds.wave_eq[wave] = q;
-      }
-      __syncthreads();
-      uint32_t pos = 0, eq_rank = 0;
-      for (int w = 0; w < wave; ++w) {
-        const uint32_t gw = lds.wave_gt[w], qw = lds.wave_eq[w];
-        pos += gw + (eq_rank < krem2 ? min(qw, krem2 - eq_rank) : 0u);
-        eq_rank += qw;
-      }
-      for (uint32_t c0l = 0; c0l < cnt; c0l += 64) {
-        const uint32_t c = c0l + lane;
-        const bool in = c < cnt;
-        const uint32_t key = in ? ckey[wave * R + c] : 0u;
-        const uint64_t be = __ballot(in && key == prefix2);
-        const uint32_t my_eq = eq_rank + lanes_below(be);
-        const bool sel = in && (key > prefix2 || (key == prefix2 && my_eq < krem2));
-        const uint64_t bs = __ballot(sel);
-        const uint32_t p = pos + lanes_below(bs);
-        if (sel && p < (uint32_t)k) {
-          oi[p] = ccol[wave * R + c];
-          if (ov) ov[p] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-        }
-        pos += __builtin_popcountll(bs);
-        eq_rank += __builtin_popcountll(be);
-      }
+      write_list(ckey, ccol, R, prefix2, krem2);
       return;
     }
     __syncthreads();  // the list is abandoned; the path below reuses its space
@@ -498,7 +681,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
   // region that would overflow sends the row down the slower path.
   uint32_t* ckey = staged ? lds.cand.key : lds.cand_long.key;
   int32_t* ccol = staged ? lds.cand.col : lds.cand_long.col;
-  const uint32_t R = (staged ? (uint32_t)kCand : (uint32_t)kCandLong) / kSelWaves;
+  const uint32_t R = (staged ? (uint32_t)kCand : (uint32_t)long_cap<kSelThreads>()) / kSelWaves;
   if (h1 != krem && h1 <= R * kSelWaves) {
     // gather bin b1; count the keys above it per wavefront
     uint32_t above = 0, mine = 0;  // mine: this wavefront's candidates so far
@@ -659,26 +842,211 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
   });
 }
 
+// The split path's plan, before the gather and the selection:
+//  * workgroup 0 orders the rows longest first (by count class, as
+//    row_of_rank; rows of one class in any order) into ws.map;
+//  * workgroup 1 + r sets row r's candidate count and, for a row not kept
+//    in LDS, the key threshold: from a sample of the row (512 of every 4096
+//    columns), the top 19 bits of the sampled key of rank
+//    ks + 5 sqrt(ks) + 5, ks = k * (sample size) / n, so that at least k
+//    keys of the row reach it but for a five-sigma miss, and about
+//    (1 + 5 / sqrt(ks)) k are expected to.  A row whose expected list would
+//    not fit kListCap slots comfortably is not split.
+template <int kSelThreads>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t rows,
+                        int32_t max_ctx, const int32_t* __restrict__ lengths,
+                        const int32_t* __restrict__ ctx, const int32_t* __restrict__ sched,
+                        int32_t batch, int32_t next_n, int32_t workers, int32_t k, SplitWs ws) {
+  __shared__ SelLds<kSelThreads> lds;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    uint8_t* cls = reinterpret_cast<uint8_t*>(lds.stage);  // class of each row
+    if (tid < kOrderBins) lds.hist[tid] = 0;
+    __syncthreads();
+    for (int32_t q = tid; q < rows; q += kSelThreads) {
+      const uint32_t c = count_class(
+          row_candidates(q, max_ctx, lengths, ctx, sched, batch, next_n, workers));
+      cls[q] = (uint8_t)c;
+      atomicAdd(&lds.hist[c], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // first rank of each class, from the top class down
+      const int lane = tid;
+      const uint32_t h0 = lds.hist[kOrderBins - 1 - 2 * lane];
+      const uint32_t h1 = lds.hist[kOrderBins - 2 - 2 * lane];
+      const uint32_t own = h0 + h1;
+      uint32_t incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      lds.hist2[kOrderBins - 1 - 2 * lane] = incl - own;
+      lds.hist2[kOrderBins - 2 - 2 * lane] = incl - own + h0;
+    }
+    __syncthreads();
+    for (int32_t q = tid; q < rows; q += kSelThreads)
+      ws.map[atomicAdd(&lds.hist2[cls[q]], 1u)] = q;
+    return;
+  }
+  const int32_t r = (int32_t)blockIdx.x - 1;
+  const int32_t n = row_candidates(r, max_ctx, lengths, ctx, sched, batch, next_n, workers);
+  uint32_t thr = kNoSplit;
+  if (n > k && n > kStage) {
+    const float* row = logits + (int64_t)r * ldo;
+    for (int j = tid; j < kBins; j += kSelThreads) lds.hist[j] = 0;
+    if (tid < kBins2) lds.hist2[tid] = 0;
+    __syncthreads();
+    for_each_sample<kSelThreads, kPlanRun>(row, lds, n, [&](int32_t col, const v4f& v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+    });
+    __syncthreads();
+    const int32_t ns = sample_size<kPlanRun>(n);
+    const float ks = (float)k * (float)ns / (float)n;
+    const float rank = ceilf(ks + 4.5f * sqrtf(ks) + 4.5f);
+    if (rank < (float)ns && rank * (float)n <= kListFill * (float)kListCap * (float)ns) {
+      const uint32_t want = (uint32_t)rank;
+      choose_bin<kSelThreads>(lds, lds.hist, kBins, want);
+      const uint32_t b = lds.chosen[0], above = lds.chosen[1];
+      __syncthreads();
+      for_each_sample<kSelThreads, kPlanRun>(row, lds, n, [&](int32_t col, const v4f& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(v[e]);
+          if (col + e < n && (key >> kTopShift) == b)
+            atomicAdd(&lds.hist2[(key >> (kTopShift - 8)) & 0xFFu], 1u);
+        }
+      });
+      __syncthreads();
+      choose_bin<kSelThreads>(lds, lds.hist2, kBins2, want - above);
+      thr = (b << kTopShift) | (lds.chosen[0] << (kTopShift - 8));
+    }
+  }
+  if (tid == 0) {
+    ws.len[r] = n;
+    ws.thr[r] = thr;
+  }
+}
+
+// The split path's gather: workgroup (r, j) takes chunk j of row r (columns
+// [jC, min(n, (j+1)C))) when the row is split and has that chunk.  Every key
+// at or above the row's threshold goes, in column order, to the chunk's
+// slots of the row's list, and the count of those keys to ws.cnt (a count
+// above the chunk's slots marks the list as not whole).
+template <int kSelThreads>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs ws) {
+  constexpr int kSelWaves = kSelThreads / 64;
+  __shared__ SelLds<kSelThreads> lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // rows start at different chunks, so that the workgroups running at once
+  // do not all read the same columns of rows a power of two apart
+  const int32_t r = (int32_t)blockIdx.x;
+  const int32_t j = (int32_t)((blockIdx.y + blockIdx.x) % gridDim.y);
+  const uint32_t thr = ws.thr[r];
+  const int32_t n = ws.len[r];
+  if (thr == kNoSplit) return;
+  const int32_t C = chunk_cols(n), nch = (n + C - 1) / C;
+  if (j >= nch) return;
+  const uint32_t R = (uint32_t)kListCap / kSelWaves;  // LDS list of each wavefront
+  uint32_t* ckey = lds.cand_long.key;
+  int32_t* ccol = lds.cand_long.col;
+  const int32_t s0 = j * C, s1 = min(n, s0 + C);
+  const int32_t lo = chunk_slot(s0, j, n), size = chunk_slot(s1, j + 1, n) - lo;
+  const int32_t L = ((s1 - s0 + kSelWaves - 1) / kSelWaves + 3) & ~3;
+  const int32_t c0 = min(s1, s0 + wave * L), c1 = min(s1, c0 + L);
+  const float* row = logits + (int64_t)r * ldo;
+  uint32_t mine = 0;
+  for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
+    uint64_t bc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bc[e] = __ballot(i + e < c1 && order_key(v[e]) >= thr);
+    uint32_t slot = mine;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (((bc[e] >> lane) & 1u) && slot < R) {
+        ckey[wave * R + slot] = order_key(v[e]);
+        ccol[wave * R + slot] = i + e;
+      }
+      slot += (bc[e] >> lane) & 1u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
+  });
+  if (lane == 0) lds.cand_cnt[wave] = mine;
+  __syncthreads();
+  uint32_t pos = 0, total = 0;
+  bool over = false;
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t m = lds.cand_cnt[w];
+    pos += w < wave ? m : 0u;
+    total += m;
+    over = over || m > R;
+  }
+  const uint32_t stored = min(mine, R);
+  const int64_t base = (int64_t)r * kRowSlots + lo;
+  for (uint32_t i = lane; i < stored; i += 64) {
+    if (pos + i < (uint32_t)size) {
+      ws.key[base + pos + i] = ckey[wave * R + i];
+      ws.col[base + pos + i] = ccol[wave * R + i];
+    }
+  }
+  if (tid == 0) ws.cnt[r * kMaxChunks + j] = over ? size + 1 : (int32_t)total;
+}
+
 }  // namespace
+
+size_t select_workspace_bytes(int32_t rows) {
+  if (rows < 1 || rows > kSplitRows) return 0;
+  const int64_t words = 3 * ws_words(rows) + ws_words((int64_t)rows * kMaxChunks) +
+                        2 * ws_words((int64_t)rows * kRowSlots);
+  return (size_t)words * 4;
+}
 
 // Workgroups of 1024 threads when every row can have one at once (two per
 // compute unit), else of 512 (four per compute unit): measured on MI355X,
 // 512 rows of up to 131072 columns select in 90-110 us with 1024 threads
 // against 104-130 us with 512, and 2048 rows of up to 65536 in 64 us with
 // 512 against 84 us with 1024.
+// With a workspace and at most two rows per compute unit, the plan and
+// gather kernels run first; the gather has a workgroup for every chunk a row
+// of max_ctx candidates could have.  With more rows every compute unit
+// already holds several rows at once, and the single kernel is faster
+// (measured on MI355X: 2048 rows of up to 65536 columns select in ~62 us
+// alone against ~68 us split, 512 rows of up to 131072 in 92-110 us alone
+// against ~73 us split).
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
-                              int32_t* out_idx, float* out_val, int64_t ldk, int32_t cus,
-                              hipStream_t stream) {
+                              int32_t* out_idx, float* out_val, int64_t ldk, void* workspace,
+                              int32_t cus, hipStream_t stream) {
+  SplitWs ws = {};
+  if (workspace && rows <= kSplitRows && (int64_t)rows <= 2 * (int64_t)cus) {
+    ws = split_ws(workspace, rows);
+    hipLaunchKernelGGL(select_plan_kernel<512>, dim3(rows + 1), dim3(512), 0, stream, logits,
+                       ldo, rows, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int32_t chunks = std::min<int32_t>(kMaxChunks, (max_ctx + kChunkMin - 1) / kChunkMin);
+    hipLaunchKernelGGL(select_gather_kernel<512>, dim3(rows, chunks), dim3(512), 0, stream,
+                       logits, ldo, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((int64_t)rows <= 2 * (int64_t)cus)
     hipLaunchKernelGGL(select_topk_kernel<1024>, dim3(rows), dim3(1024), 0, stream, logits, ldo,
                        max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
-                       ldk);
+                       ldk, ws);
   else
     hipLaunchKernelGGL(select_topk_kernel<512>, dim3(rows), dim3(512), 0, stream, logits, ldo,
                        max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
-                       ldk);
+                       ldk, ws);
   return hipGetLastError();
 }
 

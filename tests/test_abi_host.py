@@ -133,3 +133,33 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 1, 64, 128), dtype=torch.uint8)
     with pytest.raises(ValueError, match="GPU tensor"):
         pmqa.paged_mqa_logits_fp8(q, q, q, q, q, q, 16)
+
+
+def test_select_workspace_bytes():
+    """Sections of whole 256-byte blocks: map, lengths and thresholds (one
+    word per row each), chunk counts (16 words per row), keys and columns
+    (6272 words per row each: 1.5 x 3840 list slots plus 32 per chunk)."""
+    def words(n):
+        return (n + 63) // 64 * 64
+
+    for rows in (1, 5, 2048, 8192):
+        want = 4 * (3 * words(rows) + words(16 * rows) + 2 * words(6272 * rows))
+        assert pmqa.select_workspace_bytes(rows) == want, rows
+    assert pmqa.select_workspace_bytes(0) == 0
+    assert pmqa.select_workspace_bytes(8193) == 0      # no split beyond 8192 rows
+
+
+def _select(lib, ws, ws_bytes, rows=4, k=8):
+    p = ctypes.c_void_p
+    return lib.select_topk(p(FAKE), 256, rows, 256, p(FAKE), k, p(FAKE), p(FAKE), 8, p(ws),
+                           ws_bytes, p(0))
+
+
+def test_select_workspace_argument_checks():
+    lib = pmqa.library()
+    need = pmqa.select_workspace_bytes(4)
+    assert _select(lib, FAKE, need - 1) == 1
+    assert "select_workspace_bytes" in pmqa.last_error()
+    assert _select(lib, FAKE + 8, need) == 1
+    assert "16-byte aligned" in pmqa.last_error()
+    assert _select(lib, FAKE, need, k=0) == 1 and "k = 0" in pmqa.last_error()

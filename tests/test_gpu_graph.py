@@ -76,6 +76,58 @@ def test_graph_replay_tracks_context_lengths(mode):
     assert mode == "compute" or 0 < rebuilt < 6
 
 
+def test_graph_replay_fused_topk_with_split_workspace():
+    """Capture schedule + fused top-k with the split workspace (plan, gather
+    and selection kernels); lengths change in place between replays (rows
+    long enough to be split, some crossing chunk boundaries).  Every replay
+    must equal an eager call on the same lengths, bit for bit."""
+    announce("graph replay fused top-k (split workspace)")
+    B, M, k = 6, 40000, 2048
+    ctx0 = np.array([9000, 0, 16300, 30000, 7000, 38000], np.int32)
+    d = make_fp8(ctx0 + 3000, max_context_len=M, seed=81)   # pages for every step
+    dev = upload(d)
+    ctx_t = torch.from_numpy(ctx0.copy()).cuda()
+    W = pmqa.default_num_workers()
+    sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, M), dtype=torch.float32, device="cuda")
+    sws = torch.empty(pmqa.select_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    val = torch.empty((B, k), dtype=torch.float32, device="cuda")
+
+    def step(i, v, ws):
+        pmqa.compute_schedule(ctx_t, num_workers=W, out=sched)
+        pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"], ctx_t,
+                                dev["block_table"], sched, M, k, workspace=logits, indices=i,
+                                values=v, num_workers=W, select_workspace=ws)
+
+    step(idx, val, sws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(idx, val, sws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    ctx = ctx0.copy()
+    for it in range(5):
+        if it:
+            ctx = ctx + np.where(ctx > 0, 250 * it, 0).astype(np.int32)
+        ctx_t.copy_(torch.from_numpy(ctx))
+        idx.fill_(-7)                   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got_i, got_v = idx.clone(), val.clone()
+        ei = torch.empty_like(idx)
+        ev = torch.empty_like(val)
+        step(ei, ev, None)              # eager, single-kernel selection
+        torch.cuda.synchronize()
+        assert torch.equal(got_i, ei), it
+        assert torch.equal(got_v.view(torch.int32), ev.view(torch.int32)), it
+
+
 def test_validate_mode_detects_stale_schedule(monkeypatch):
     announce("validate: stale schedule")
     d = make_fp8([100, 250, 0], max_context_len=600, seed=81)

@@ -21,11 +21,24 @@ def _rows(rng, rows, M, pool):
     return (rng.standard_normal((rows, M)) * 10).astype(np.float32)
 
 
+# "auto": the binding passes a workspace (rows ordered by the plan kernel,
+# long rows split over workgroups); None: the single-kernel path.
+WS = ["auto", None]
+
+
+def _check_rows(x, n, k, idx, val):
+    for r in range(x.shape[0]):
+        wi, wv = otk.select_topk(x[r], max(0, int(n[r])), k)
+        assert np.array_equal(idx[r], wi), r
+        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+
+
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("pool", [False, True])
 @pytest.mark.parametrize("M,stride,k", [(1, 4, 1), (37, 40, 5), (1000, 1024, 7),
                                         (5000, 5004, 2048), (3000, 3000, 2999)])
-def test_select_topk_matches_oracle(pool, M, stride, k):
-    announce(f"select_topk M={M} k={k} pool={pool}")
+def test_select_topk_matches_oracle(pool, M, stride, k, ws):
+    announce(f"select_topk M={M} k={k} pool={pool} ws={ws}")
     rng = np.random.default_rng(M + k + pool)
     rows = 64
     x = _rows(rng, rows, M, pool)
@@ -34,41 +47,38 @@ def test_select_topk_matches_oracle(pool, M, stride, k):
     n[5] = -3                                      # clamped to 0
     buf = torch.full((rows, stride), float("nan"), device="cuda")
     buf[:, :M] = torch.from_numpy(x).cuda()        # NaN past the width: never read
-    idx, val = pmqa.select_topk(buf[:, :M], torch.from_numpy(n).cuda(), k)
-    idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    for r in range(rows):
-        wi, wv = otk.select_topk(x[r], max(0, int(n[r])), k)
-        assert np.array_equal(idx[r], wi), r
-        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+    idx, val = pmqa.select_topk(buf[:, :M], torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("rows", [3000, 8192, 8193])
-def test_select_topk_many_rows(rows):
+def test_select_topk_many_rows(rows, ws):
     """Workgroups take rows longest first (by count class) up to 8192 rows,
     in index order beyond: every row is still selected exactly once, with
     lengths spread over many classes and many rows per class."""
-    announce(f"select_topk rows={rows}")
+    announce(f"select_topk rows={rows} ws={ws}")
     rng = np.random.default_rng(rows)
     M, k = 300, 17
     x = (rng.standard_normal((rows, M)) * 3).astype(np.float32)
     n = rng.integers(0, M + 1, size=rows).astype(np.int32)
     n[rng.random(rows) < 0.3] = 40                 # a crowded class
     n[::97] = 0
-    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k)
-    idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    for r in range(rows):
-        wi, wv = otk.select_topk(x[r], int(n[r]), k)
-        assert np.array_equal(idx[r], wi), r
-        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
-def test_select_topk_long_rows_sample_misses_and_overflows():
+@pytest.mark.parametrize("ws", WS)
+def test_select_topk_long_rows_sample_misses_and_overflows(ws):
     """Rows too long for LDS are sampled (256 of every 4096 columns) to guess
     the bins of the k-th key.  An unrepresentative sample (the columns it
     reads hold only small values) and a gathered list that overflows one
     wavefront's share (every large value in the first eighth of the row)
-    must both fall back to the exact three-pass path."""
-    announce("select_topk sample misses / overflow")
+    must both fall back to the exact three-pass path.  With the split
+    workspace the same rows overflow their chunk lists and fall back too."""
+    announce(f"select_topk sample misses / overflow ws={ws}")
     rng = np.random.default_rng(21)
     rows, M, k = 4, 65536, 2048
     x = rng.standard_normal((rows, M)).astype(np.float32)
@@ -76,31 +86,92 @@ def test_select_topk_long_rows_sample_misses_and_overflows():
     x[0, sampled] -= np.float32(100.0)              # the sample sees only small values
     x[1, : M // 8] += np.float32(10.0)              # all large values in one chunk
     n = np.array([M, M, M, 7681], np.int32)
-    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k)
-    idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    for r in range(rows):
-        wi, wv = otk.select_topk(x[r], int(n[r]), k)
-        assert np.array_equal(idx[r], wi), r
-        assert np.array_equal(val[r].view(np.uint32), wv.view(np.uint32)), r
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
-def test_select_topk_long_rows():
-    announce("select_topk 131072 columns")
+@pytest.mark.parametrize("ws", WS)
+def test_select_topk_long_rows(ws):
+    announce(f"select_topk 131072 columns ws={ws}")
     rng = np.random.default_rng(9)
     rows, M, k = 6, 131072, 2048
     x = (rng.standard_normal((rows, M))).astype(np.float32)
     x[1] = np.float32(0.5)                         # all equal: the first k columns
     x[2, ::3] = np.float32(4.0)                    # many ties above the rest
     n = np.array([M, M, M, 70001, 2049, 2048], np.int32)
-    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k)
-    idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    for r in range(rows):
-        wi, wv = otk.select_topk(x[r], int(n[r]), k)
-        assert np.array_equal(idx[r], wi), r
-        assert np.array_equal(val[r], wv), r
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
-def _fused(d, k, dev=None, num_workers=None, schedule=None):
+@pytest.mark.parametrize("k", [1, 100, 2048, 3000])
+def test_select_topk_split_rows(k):
+    """The split path: lengths around the chunk boundaries (one chunk up to
+    8192 columns, 16 chunks from 131072, wider chunks beyond), values with
+    many ties at the k-th key, signed zeros and -inf.  k = 3000 expects too
+    long a list, so those rows are not split."""
+    announce(f"select_topk split rows k={k}")
+    rng = np.random.default_rng(31 + k)
+    M = 200000
+    lens = [7681, 8192, 8193, 9000, 16385, 65536, 131072, 131073, 200000]
+    rows = len(lens) + 2
+    x = rng.standard_normal((rows, M)).astype(np.float32)
+    x[1] = np.round(x[1] * 64) / 64                 # ties at the k-th key
+    x[2, ::5] = np.float32(-0.0)
+    x[2, 1::5] = np.float32(0.0)
+    x[3, ::7] = -np.inf
+    x[-2] = np.round(x[-2] * 8) / 8                 # few levels: lists overflow
+    x[-1] = np.linspace(-1, 1, M, dtype=np.float32)  # the largest keys in the last chunk
+    n = np.array(lens + [131072, 131072], np.int32)
+    buf = torch.from_numpy(x).cuda()
+    lens_t = torch.from_numpy(n).cuda()
+    ws = torch.empty(pmqa.select_workspace_bytes(rows), dtype=torch.uint8, device="cuda")
+    idx, val = pmqa.select_topk(buf, lens_t, k, select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+    thr, cnt = _split_state(ws, rows)
+    split = thr != 0xFFFFFFFF
+    if k == 2048:   # the plain normal rows take the split path with whole lists
+        for r in (0, 4, 5, 6, 7, 8):
+            assert split[r], r
+            nch = -(-int(n[r]) // _chunk_cols(int(n[r])))
+            assert 2048 <= cnt[r, :nch].sum() <= 3840, (r, cnt[r, :nch])
+    if k in (1, 100):
+        assert split[0] and split[8]
+    if k == 3000:
+        assert not split.any()
+
+
+def _chunk_cols(n):
+    return max(16384, -(-n // 16384) * 1024)
+
+
+def _split_state(ws, rows):
+    """Thresholds [rows] and chunk counts [rows, 16] the split path left in
+    its workspace (sections of whole 256-byte blocks: map, lengths,
+    thresholds, counts, keys, columns)."""
+    w = ws.view(torch.int32).cpu().numpy()
+    blk = -(-rows // 64) * 64
+    thr = w[2 * blk: 2 * blk + rows].view(np.uint32)
+    return thr, w[3 * blk: 3 * blk + 16 * rows].reshape(rows, 16)
+
+
+def test_select_workspace_reused_across_calls():
+    """One workspace for two calls in a row, the second with fewer rows and
+    shorter lengths: nothing of the first call's lists leaks into it."""
+    announce("select_topk workspace reuse")
+    rng = np.random.default_rng(41)
+    ws = torch.empty(pmqa.select_workspace_bytes(12), dtype=torch.uint8, device="cuda")
+    k = 2048
+    for rows, M in ((12, 100000), (5, 40000)):
+        x = rng.standard_normal((rows, M)).astype(np.float32)
+        n = rng.integers(M // 2, M + 1, size=rows).astype(np.int32)
+        idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                    select_workspace=ws)
+        _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+
+
+def _fused(d, k, dev=None, num_workers=None, schedule=None, ws="auto"):
     dev = upload(d) if dev is None else dev
     nn = int(d["next_n"])
     fp8 = d["variant"] == "fp8"
@@ -112,12 +183,12 @@ def _fused(d, k, dev=None, num_workers=None, schedule=None):
     if fp8:
         idx, val = pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
                                            dev["context_lens"], dev["block_table"], schedule, M,
-                                           k, num_workers=num_workers)
+                                           k, num_workers=num_workers, select_workspace=ws)
     else:
         idx, val = pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"],
                                            dev["weights"], dev["context_lens"],
                                            dev["block_table"], schedule, M, k,
-                                           num_workers=num_workers)
+                                           num_workers=num_workers, select_workspace=ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), val.cpu().numpy()
 
@@ -131,10 +202,11 @@ def _row_lengths(d, rows=None):
                                           c[r // nn]) for r in rows])
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("variant", ["fp8", "fp4"])
 @pytest.mark.parametrize("next_n", [1, 2])
-def test_fused_topk_against_oracle(variant, next_n):
-    announce(f"fused top-k {variant} next_n={next_n}")
+def test_fused_topk_against_oracle(variant, next_n, ws):
+    announce(f"fused top-k {variant} next_n={next_n} ws={ws}")
     rng = np.random.default_rng(20 + next_n)
     ctx = rng.integers(0, 3000, size=40)
     ctx[::6] = 0
@@ -145,8 +217,43 @@ def test_fused_topk_against_oracle(variant, next_n):
            bt_stride=-(-3500 // 64))
     ref = oracle(d)
     for k in (1, 100, 1024):
+        idx, val = _fused(d, k, ws=ws)
+        parity.check_topk(idx, val, ref, _row_lengths(d), k, f"{variant} k={k}")
+
+
+@pytest.mark.parametrize("variant", ["fp8", "fp4"])
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_fused_topk_split_rows(variant, next_n):
+    """Rows too long for LDS (split over workgroups with the workspace) in
+    the fused step, whose candidate counts come from the schedule."""
+    announce(f"fused top-k split rows {variant} next_n={next_n}")
+    ctx = np.array([0, 7700, 8193, 20000, 33000, 5000, 41000, 1], np.int64)
+    mk = make_fp8 if variant == "fp8" else make_fp4
+    d = mk(ctx, next_n=next_n, max_context_len=40000, seed=50 + next_n,
+           bt_stride=-(-41000 // 64))
+    ref = oracle(d)
+    dev = upload(d)
+    nn, M = int(d["next_n"]), int(d["max_context_len"])
+    lens = torch.from_numpy(_row_lengths(d).astype(np.int32)).cuda()
+    for k in (64, 2048):
         idx, val = _fused(d, k)
         parity.check_topk(idx, val, ref, _row_lengths(d), k, f"{variant} k={k}")
+        # the same logits, selected by the single-kernel path: bit for bit
+        logits = torch.empty((len(ctx) * nn, M), device="cuda")
+        sched = pmqa.compute_schedule(dev["context_lens"], next_n=nn,
+                                      variant=pmqa.VARIANT_FP8 if variant == "fp8"
+                                      else pmqa.VARIANT_FP4)
+        if variant == "fp8":
+            i2, v2 = pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                             dev["context_lens"], dev["block_table"], sched, M,
+                                             k, workspace=logits)
+        else:
+            i2, v2 = pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"],
+                                             dev["weights"], dev["context_lens"],
+                                             dev["block_table"], sched, M, k, workspace=logits)
+        i1, v1 = pmqa.select_topk(logits, lens, k, select_workspace=None)
+        assert torch.equal(i1, i2) and torch.equal(v1.view(torch.int32), v2.view(torch.int32))
+        assert np.array_equal(idx, i2.cpu().numpy())
 
 
 def test_fused_topk_mismatched_schedule_selects_nothing():
