@@ -251,11 +251,11 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
  *                   pmqa_select_workspace_bytes(rows) bytes, 16-byte aligned,
  *                   owned by the caller, contents unspecified before and
  *                   after the call (error PMQA_ERR_INVALID_ARGUMENT when
- *                   smaller or misaligned).  With it, the rows too long to
- *                   be kept in LDS are split into chunks over many
- *                   workgroups (two more kernels run first); the result is
- *                   the same.  Calls that share one workspace must be
- *                   ordered (one stream).
+ *                   smaller or misaligned).  With it, and at most 512 rows,
+ *                   the rows too long to be kept in LDS are split into
+ *                   chunks over many workgroups (two more kernels run
+ *                   first); the result is the same.  Calls that share one
+ *                   workspace must be ordered (one stream).
  *   select_workspace_bytes  its size.
  *
  * One workgroup per row for the final selection; no host synchronization;
@@ -270,7 +270,7 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
 /*
  * pmqa_select_workspace_bytes - bytes of the optional select_workspace of
  * select_topk and paged_mqa_topk_fp8/fp4 for `rows` rows (about 49 KB per
- * row); 0 when no workspace would be used (rows < 1 or rows > 8192).
+ * row); 0 when no workspace would be used (rows < 1 or rows > 512).
  * Host-only arithmetic.
  */
 size_t pmqa_select_workspace_bytes(int32_t rows);

@@ -73,7 +73,7 @@ hipError_t launch_append(int variant, const void* k, int32_t dtype, int64_t n,
 // select_workspace_bytes(rows) bytes, 16-byte aligned (unused for more than
 // kSplitRows rows); with it, long rows are split over several workgroups.
 // cus: compute units of the device.
-constexpr int32_t kSplitRows = 8192;
+constexpr int32_t kSplitRows = 512;  // two rows per compute unit of an MI355X
 size_t select_workspace_bytes(int32_t rows);
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,

@@ -47,8 +47,8 @@
 // workgroup derives its row from the counts of all rows (for up to 8192
 // rows; beyond that workgroup i takes row i).
 //
-// Split rows.  With a workspace and few rows (at most two per compute unit,
-// so one workgroup per row would leave most of the chip waiting on the
+// Split rows.  With a workspace and few rows (at most 512, two per compute
+// unit, so one workgroup per row would leave most of the chip waiting on the
 // longest rows), two kernels run before the selection:
 //   * the plan orders the rows once for all workgroups (ws.map) and gives
 //     each row not kept in LDS a key threshold from a sample of the row,
@@ -129,7 +129,7 @@ __device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
   return (int32_t)max((int64_t)0, min(min(lim, (int64_t)kUnit * c), (int64_t)max_ctx));
 }
 
-constexpr int kOrderRows = kSplitRows;    // rows ordered longest first
+constexpr int kOrderRows = 8192;          // rows ordered longest first
 constexpr int kOrderBins = 128;           // count classes
 
 // Columns of each chunk of a split row of n candidates: at least kChunkMin,
@@ -1014,20 +1014,20 @@ size_t select_workspace_bytes(int32_t rows) {
 // 512 rows of up to 131072 columns select in 90-110 us with 1024 threads
 // against 104-130 us with 512, and 2048 rows of up to 65536 in 64 us with
 // 512 against 84 us with 1024.
-// With a workspace and at most two rows per compute unit, the plan and
-// gather kernels run first; the gather has a workgroup for every chunk a row
-// of max_ctx candidates could have.  With more rows every compute unit
-// already holds several rows at once, and the single kernel is faster
-// (measured on MI355X: 2048 rows of up to 65536 columns select in ~62 us
-// alone against ~68 us split, 512 rows of up to 131072 in 92-110 us alone
-// against ~73 us split).
+// With a workspace and at most kSplitRows rows (two per compute unit), the
+// plan and gather kernels run first; the gather has a workgroup for every
+// chunk a row of max_ctx candidates could have.  With more rows every
+// compute unit already holds several rows at once, and the single kernel is
+// faster (measured on MI355X: 2048 rows of up to 65536 columns select in
+// ~62 us alone against ~68 us split, 512 rows of up to 131072 in 92-113 us
+// alone against 61-67 us split).
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
                               int32_t* out_idx, float* out_val, int64_t ldk, void* workspace,
                               int32_t cus, hipStream_t stream) {
   SplitWs ws = {};
-  if (workspace && rows <= kSplitRows && (int64_t)rows <= 2 * (int64_t)cus) {
+  if (workspace && rows <= kSplitRows) {
     ws = split_ws(workspace, rows);
     hipLaunchKernelGGL(select_plan_kernel<512>, dim3(rows + 1), dim3(512), 0, stream, logits,
                        ldo, rows, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, ws);

@@ -53,7 +53,7 @@ def test_select_topk_matches_oracle(pool, M, stride, k, ws):
 
 
 @pytest.mark.parametrize("ws", WS)
-@pytest.mark.parametrize("rows", [3000, 8192, 8193])
+@pytest.mark.parametrize("rows", [512, 513, 3000, 8192, 8193])
 def test_select_topk_many_rows(rows, ws):
     """Workgroups take rows longest first (by count class) up to 8192 rows,
     in index order beyond: every row is still selected exactly once, with
@@ -107,14 +107,15 @@ def test_select_topk_long_rows(ws):
 
 @pytest.mark.parametrize("k", [1, 100, 2048, 3000])
 def test_select_topk_split_rows(k):
-    """The split path: lengths around the chunk boundaries (one chunk up to
-    8192 columns, 16 chunks from 131072, wider chunks beyond), values with
-    many ties at the k-th key, signed zeros and -inf.  k = 3000 expects too
-    long a list, so those rows are not split."""
+    """The split path: lengths around the chunk boundaries (chunks of 16384
+    columns, one chunk up to 16384, a last chunk of one column, 16 wider
+    chunks from 262144), values with many ties at the k-th key, signed
+    zeros and -inf.  k = 3000 expects too long a list, so those rows are
+    not split."""
     announce(f"select_topk split rows k={k}")
     rng = np.random.default_rng(31 + k)
-    M = 200000
-    lens = [7681, 8192, 8193, 9000, 16385, 65536, 131072, 131073, 200000]
+    M = 300000
+    lens = [7681, 8192, 8193, 9000, 16385, 65536, 131072, 131073, 200000, 262145, 300000]
     rows = len(lens) + 2
     x = rng.standard_normal((rows, M)).astype(np.float32)
     x[1] = np.round(x[1] * 64) / 64                 # ties at the k-th key
@@ -132,12 +133,12 @@ def test_select_topk_split_rows(k):
     thr, cnt = _split_state(ws, rows)
     split = thr != 0xFFFFFFFF
     if k == 2048:   # the plain normal rows take the split path with whole lists
-        for r in (0, 4, 5, 6, 7, 8):
+        for r in (0, 4, 5, 6, 7, 8, 9, 10):
             assert split[r], r
             nch = -(-int(n[r]) // _chunk_cols(int(n[r])))
             assert 2048 <= cnt[r, :nch].sum() <= 3840, (r, cnt[r, :nch])
     if k in (1, 100):
-        assert split[0] and split[8]
+        assert split[0] and split[10]
     if k == 3000:
         assert not split.any()
 
