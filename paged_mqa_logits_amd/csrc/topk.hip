@@ -1014,9 +1014,10 @@ size_t select_workspace_bytes(int32_t rows) {
 // 512 rows of up to 131072 columns select in 90-110 us with 1024 threads
 // against 104-130 us with 512, and 2048 rows of up to 65536 in 64 us with
 // 512 against 84 us with 1024.
-// With a workspace and at most kSplitRows rows (two per compute unit), the
-// plan and gather kernels run first; the gather has a workgroup for every
-// chunk a row of max_ctx candidates could have.  With more rows every
+// With a workspace, at most kSplitRows rows (two per compute unit) and rows
+// that may be too long for LDS, the plan and gather kernels run first; the
+// gather has a workgroup for every chunk a row of max_ctx candidates could
+// have.  With more rows every
 // compute unit already holds several rows at once, and the single kernel is
 // faster (measured on MI355X: 2048 rows of up to 65536 columns select in
 // ~62 us alone against ~68 us split, 512 rows of up to 131072 in 92-113 us
@@ -1027,7 +1028,7 @@ hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, in
                               int32_t* out_idx, float* out_val, int64_t ldk, void* workspace,
                               int32_t cus, hipStream_t stream) {
   SplitWs ws = {};
-  if (workspace && rows <= kSplitRows) {
+  if (workspace && rows <= kSplitRows && max_ctx > kStage && max_ctx > k) {
     ws = split_ws(workspace, rows);
     hipLaunchKernelGGL(select_plan_kernel<512>, dim3(rows + 1), dim3(512), 0, stream, logits,
                        ldo, rows, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, ws);
