@@ -72,6 +72,8 @@ constexpr int kScaleOne = 127;  // E8M0 encoding of 1.0
 constexpr int kRsrcWord3 = 0x00020000;
 // Cache-policy bits of a streaming (non-temporal) buffer load.
 constexpr int kLoadNT = 2;
+// Cache-policy bits of a non-temporal store.
+constexpr int kStoreNT = 2;
 // Cache-policy bits of the logit stores: SC1 (device scope).  Measured on
 // MI355X, stores issued this way slow the K stream less than plain or
 // non-temporal ones (large_fp8 call -6 us, mxfp4 -14 us).
@@ -549,6 +551,34 @@ __device__ __forceinline__ void flush_stage(const LogitsArgs& a, const float* st
   }
 }
 
+// -inf over piece `piece` of `pieces` of output row r's columns that no
+// unit covers ([256 c_b, max_ctx), c_b the unit count of its batch row b
+// from prefix sums s0 = S[b], s1 = S[b+1]; the whole row when the schedule
+// is unusable).  Used for small outputs instead of the separate fill kernel:
+// those columns are disjoint from every unit's, so no order is needed.
+__device__ __forceinline__ void fill_tail(const LogitsArgs& a, const SchedView& v, int32_t r,
+                                          int32_t piece, int32_t pieces, int32_t s0,
+                                          int32_t s1, int lane) {
+  const int32_t c = v.rows ? min(max(s1 - s0, 0), v.cap) : 0;
+  const int32_t start = min(c * kUnit, a.max_ctx);
+  const int32_t per = ((a.max_ctx - start + pieces - 1) / pieces + 3) & ~3;
+  const int32_t c0 = min(a.max_ctx, start + piece * per), c1 = min(a.max_ctx, c0 + per);
+  const rsrc_t orow = make_rsrc(a.out + (int64_t)r * a.ldo, 4u * (uint32_t)a.max_ctx);
+  const float ninf = -__builtin_inff();
+  const v4f nv = {ninf, ninf, ninf, ninf};
+  for (int32_t col = c0 + 4 * lane; col < c1; col += 256) {
+    if (col + 4 <= c1) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, nv), orow,
+                                             (int32_t)(4u * (uint32_t)col), 0, kStoreNT);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (col + e < c1)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(ninf), orow,
+                                                (int32_t)(4u * (uint32_t)(col + e)), 0, kStoreNT);
+    }
+  }
+}
+
 template <class Fmt, int NN, int HG>
 __global__ __launch_bounds__(kBlockThreads)
 __attribute__((amdgpu_waves_per_eu(Fmt::waves_per_simd(NN, HG), Fmt::waves_per_simd(NN, HG))))
@@ -568,8 +598,21 @@ void logits_kernel(const LogitsArgs a) {
   const int32_t start_b = sload(range), start_u = sload(range + 1);
   const int32_t end_b = sload(range + 2), end_u = sload(range + 3);
   const SchedView v = make_view(a);
-  __asm__ volatile("" ::"s"(start_b), "s"(start_u), "s"(end_b), "s"(end_u), "s"(v.rows));
-  if (v.rows == 0) return;
+  // Small outputs: the workers also write -inf past every row's units, the
+  // R output rows dealt out as R * (W / R) pieces (R <= W, checked by the
+  // launcher); the prefix sums of the piece's row come with the range.
+  const int32_t out_rows = a.batch * NN;
+  const int32_t fr = wid % out_rows, fpiece = wid / out_rows;
+  const int32_t fpieces = a.num_workers / out_rows;
+  const bool fill = a.fill_tails && fpiece < fpieces;
+  const int32_t fs0 = fill ? sload(v.S + fr / NN) : 0;
+  const int32_t fs1 = fill ? sload(v.S + fr / NN + 1) : 0;
+  __asm__ volatile("" ::"s"(start_b), "s"(start_u), "s"(end_b), "s"(end_u), "s"(v.rows),
+                   "s"(fs0), "s"(fs1));
+  if (v.rows == 0) {
+    if (fill) fill_tail(a, v, fr, fpiece, fpieces, fs0, fs1, lane);
+    return;
+  }
   float* stage = stage_all[wave];
   int32_t* meta = meta_all[wave];
   uint8_t* xpose = xpose_all[wave];
@@ -579,7 +622,10 @@ void logits_kernel(const LogitsArgs a) {
   it.end_b = end_b;
   it.end_u = end_u;
   Unit cur = it.first(start_b, start_u);
-  if (!it.valid(cur)) return;
+  if (!it.valid(cur)) {
+    if (fill) fill_tail(a, v, fr, fpiece, fpieces, fs0, fs1, lane);
+    return;
+  }
   const int32_t rows = v.rows;
   // The first row's query block and weights are requested before the first
   // pages, so waiting for them does not wait for the pages too.
@@ -590,6 +636,8 @@ void logits_kernel(const LogitsArgs a) {
   typename Fmt::KFrag ring[kPagesPerUnit];
 #pragma unroll
   for (int p = 0; p < kPagesPerUnit; ++p) load_page<Fmt>(a, cur, p, rows, lane, ring[p]);
+  // the -inf stores go out while the first pages are on their way
+  if (fill) fill_tail(a, v, fr, fpiece, fpieces, fs0, fs1, lane);
   int32_t staged = 0;
   uint32_t phase = flush_phase(a.flush_ticks);
   // One exit, after the flush of the last unit, so the load counter has the

@@ -38,6 +38,7 @@ struct LogitsArgs {
   int32_t max_ctx;
   int32_t num_workers;
   uint32_t flush_ticks;     // period of the synchronised stage flushes (set by the launcher)
+  int32_t fill_tails;       // 1: the unit kernel also writes -inf past every row's units
 };
 
 // Launchers (defined next to their kernels).  Return the launch status.

@@ -1,4 +1,6 @@
-// -inf fill of the logits region, run before the unit kernel.
+// -inf fill of the logits region, run before the unit kernel (for outputs
+// above 32 MB; smaller ones are filled past their units by the unit
+// kernel's own workers).
 //
 // Page "[flashinfer] Blackwell 아키텍처를 위한 고성능 Paged MQA Logits 커널 도입",
 // introduction: positions past a row's context carry no score; they are -inf
