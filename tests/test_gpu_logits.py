@@ -127,6 +127,22 @@ def test_tail_columns_covered():
         parity.check(lg, ref, f"tail coverage W={W}")
 
 
+def test_tail_fill_pieces():
+    """Small outputs get their -inf past the units from the unit kernel's
+    workers, R output rows dealt out in W // R pieces: R == W, R < W with
+    idle workers, many pieces per row, and R > W (the separate fill), on a
+    poisoned output of a width that is not a multiple of 4."""
+    announce("in-kernel tail fill pieces")
+    M = 1001
+    ctx = np.array([0, 300, 1001, 1500, 17], np.int64)
+    d = make_fp8(ctx, next_n=2, max_context_len=M, seed=76, bt_stride=-(-1500 // 64))
+    ref = oracle(d)
+    dev = upload(d)
+    for W in (10, 11, 37, 1024, 9):
+        lg, _ = run(d, dev=dev, num_workers=W)
+        parity.check(lg, ref, f"tail fill W={W}")
+
+
 def test_large_batch_of_short_rows():
     """16385 batch rows, most of them empty: the schedule's prefix sums no
     longer fit its LDS table and are searched in global memory."""
