@@ -380,7 +380,7 @@ def main():
     ws = torch.empty_like(out)
     tk_idx = torch.empty((B * NN, K_TOP), dtype=torch.int32, device="cuda")
     tk_val = torch.empty((B * NN, K_TOP), dtype=torch.float32, device="cuda")
-    sel_bytes = pmqa.select_workspace_bytes(B * NN)
+    sel_bytes = pmqa.select_workspace_bytes(B * NN, M, K_TOP)
     sel_ws = torch.empty(sel_bytes, dtype=torch.uint8, device="cuda") if sel_bytes else None
 
     def topk_call():

@@ -248,7 +248,8 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
  *   topk_values     fp32 [rows, topk_stride] or NULL.
  *   topk_stride     >= k.
  *   select_workspace        NULL, or a device buffer of at least
- *                   pmqa_select_workspace_bytes(rows) bytes, 16-byte aligned,
+ *                   pmqa_select_workspace_bytes(rows, max_context_len, k)
+ *                   bytes, 16-byte aligned,
  *                   owned by the caller, contents unspecified before and
  *                   after the call (error PMQA_ERR_INVALID_ARGUMENT when
  *                   smaller or misaligned).  With it, and at most 512 rows,
@@ -269,11 +270,13 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
 
 /*
  * pmqa_select_workspace_bytes - bytes of the optional select_workspace of
- * select_topk and paged_mqa_topk_fp8/fp4 for `rows` rows (about 49 KB per
- * row); 0 when no workspace would be used (rows < 1 or rows > 512).
+ * select_topk and paged_mqa_topk_fp8/fp4 for `rows` rows of at most
+ * max_context_len candidates and this k (about 49 KB per row); 0 when no
+ * workspace would be used: rows < 1 or rows > 512, or no row can be too
+ * long for one workgroup's LDS (max_context_len <= 7680 or <= k).
  * Host-only arithmetic.
  */
-size_t pmqa_select_workspace_bytes(int32_t rows);
+size_t pmqa_select_workspace_bytes(int32_t rows, int32_t max_context_len, int32_t k);
 
 /*
  * paged_mqa_topk_fp8 / paged_mqa_topk_fp4 - the indexer step: logits of

@@ -16,7 +16,7 @@ Entry points (same names as the C ABI):
     paged_mqa_logits_fp4(q, q_scale, kv_cache, weights, context_lens,
                          block_table, schedule, max_context_len, out=None)
     select_topk(logits, lengths, k) -> (indices, values)
-    select_workspace_bytes(rows)
+    select_workspace_bytes(rows, max_context_len, k)
     paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table,
                        schedule, max_context_len, k) -> (indices, values)
     paged_mqa_topk_fp4(q, q_scale, kv_cache, ..., k) -> (indices, values)
@@ -90,7 +90,7 @@ _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i
 _lib.select_topk.restype = ctypes.c_int
 _lib.select_topk.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p, _sz, _p]
 _lib.pmqa_select_workspace_bytes.restype = _sz
-_lib.pmqa_select_workspace_bytes.argtypes = [_i32]
+_lib.pmqa_select_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.paged_mqa_topk_fp8.restype = ctypes.c_int
 _lib.paged_mqa_topk_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _i64, _p, _sz,
                                     _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i64, _i32,
@@ -303,12 +303,12 @@ def _topk_out(indices, values, rows, k, want_values, device):
     return indices, values, indices.stride(0)
 
 
-def select_workspace_bytes(rows):
-    """Bytes of the optional top-k split workspace for `rows` rows (0: none used)."""
-    return int(_lib.pmqa_select_workspace_bytes(int(rows)))
+def select_workspace_bytes(rows, max_context_len, k):
+    """Bytes of the optional top-k split workspace (0: none would be used)."""
+    return int(_lib.pmqa_select_workspace_bytes(int(rows), int(max_context_len), int(k)))
 
 
-def _select_ws(select_workspace, rows, device):
+def _select_ws(select_workspace, rows, max_context_len, k, device):
     """(pointer, bytes) of the top-k split workspace: "auto" allocates one,
     None passes none, a uint8 tensor is used as given."""
     if select_workspace is None:
@@ -316,7 +316,7 @@ def _select_ws(select_workspace, rows, device):
     if isinstance(select_workspace, str):
         if select_workspace != "auto":
             raise ValueError('select_workspace must be "auto", None or a tensor')
-        n = select_workspace_bytes(rows)
+        n = select_workspace_bytes(rows, max_context_len, k)
         if n == 0:
             return None, 0
         select_workspace = torch.empty(n, dtype=torch.uint8, device=device)
@@ -329,7 +329,8 @@ def select_topk(logits, lengths, k, indices=None, values=None, want_values=True,
     """Top k of each row's first lengths[r] columns, ascending column order;
     returns (indices int32 [rows, k], values fp32 [rows, k] or None).
     select_workspace: "auto" (allocated here), None (single-kernel path) or a
-    uint8 tensor of at least select_workspace_bytes(rows) bytes."""
+    uint8 tensor of at least select_workspace_bytes(rows, max_context_len, k)
+    bytes."""
     _need(logits, "logits", (torch.float32,), ndim=2, contiguous=False)
     _need(lengths, "lengths", (torch.int32,), ndim=1)
     rows, M = logits.shape
@@ -338,7 +339,7 @@ def select_topk(logits, lengths, k, indices=None, values=None, want_values=True,
     if lengths.shape[0] != rows:
         raise ValueError("lengths must have one entry per row")
     indices, values, ldk = _topk_out(indices, values, rows, int(k), want_values, logits.device)
-    ws, ws_bytes = _select_ws(select_workspace, rows, logits.device)
+    ws, ws_bytes = _select_ws(select_workspace, rows, M, int(k), logits.device)
     _check(_lib.select_topk(_ptr(logits), logits.stride(0), rows, M, _ptr(lengths), int(k),
                             _ptr(indices), _ptr(values), ldk, _ptr(ws), ws_bytes,
                             _stream_ptr(stream)))
@@ -356,7 +357,7 @@ def paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table, schedule
     W = _sched_workers(schedule, B, num_workers)
     _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
     indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
-    ws, ws_bytes = _select_ws(select_workspace, B * NN, q.device)
+    ws, ws_bytes = _select_ws(select_workspace, B * NN, int(max_context_len), int(k), q.device)
     _check(_lib.paged_mqa_topk_fp8(
         _ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens), _ptr(block_table),
         _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk, _ptr(ws), ws_bytes,
@@ -375,7 +376,7 @@ def paged_mqa_topk_fp4(q, q_scale, kv_cache, weights, context_lens, block_table,
     W = _sched_workers(schedule, B, num_workers)
     _, ldo, buf = _logits_out(workspace, B * NN, int(max_context_len), q.device)
     indices, values, ldk = _topk_out(indices, values, B * NN, int(k), want_values, q.device)
-    ws, ws_bytes = _select_ws(select_workspace, B * NN, q.device)
+    ws, ws_bytes = _select_ws(select_workspace, B * NN, int(max_context_len), int(k), q.device)
     _check(_lib.paged_mqa_topk_fp4(
         _ptr(q), _ptr(q_scale), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
         _ptr(block_table), _ptr(schedule), _ptr(buf), int(k), _ptr(indices), _ptr(values), ldk,

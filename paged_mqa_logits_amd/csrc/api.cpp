@@ -439,7 +439,7 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
 namespace {
 
 pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, int64_t ldk,
-                             int32_t rows, const void* ws, size_t ws_bytes) {
+                             int32_t rows, int32_t max_ctx, const void* ws, size_t ws_bytes) {
   if (k < 1) return fail(PMQA_ERR_INVALID_ARGUMENT, "k = %d must be >= 1", k);
   if (!idx) return fail(PMQA_ERR_INVALID_ARGUMENT, "topk_indices is null");
   if (!aligned(idx, 4) || (val && !aligned(val, 4)))
@@ -450,7 +450,7 @@ pmqa_status_t check_topk_out(int32_t k, const int32_t* idx, const float* val, in
   if (ws) {
     if (!aligned(ws, 16))
       return fail(PMQA_ERR_INVALID_ARGUMENT, "select_workspace must be 16-byte aligned");
-    const size_t need = pmqa::select_workspace_bytes(rows);
+    const size_t need = pmqa::select_workspace_bytes(rows, max_ctx, k);
     if (ws_bytes < need)
       return fail(PMQA_ERR_INVALID_ARGUMENT,
                   "select_workspace_bytes = %zu < %zu needed for %d rows", ws_bytes, need, rows);
@@ -465,7 +465,7 @@ pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const
                           const Shape& s, int32_t num_heads, int32_t head_dim, int32_t page_size,
                           hipStream_t stream) {
   const int32_t rows = (int32_t)std::min<int64_t>((int64_t)s.batch * s.next_n, INT32_MAX);
-  pmqa_status_t st = check_topk_out(k, idx, val, ldk, rows, sel_ws, sel_ws_bytes);
+  pmqa_status_t st = check_topk_out(k, idx, val, ldk, rows, s.max_ctx, sel_ws, sel_ws_bytes);
   if (st != PMQA_OK) return st;
   st = logits_common(variant, q, q_scale, kv, weights, ctx, bt, sched, workspace, s, num_heads,
                      head_dim, page_size, stream, /*fill=*/false);
@@ -482,7 +482,9 @@ pmqa_status_t topk_common(int variant, const void* q, const void* q_scale, const
 
 }  // namespace
 
-size_t pmqa_select_workspace_bytes(int32_t rows) { return pmqa::select_workspace_bytes(rows); }
+size_t pmqa_select_workspace_bytes(int32_t rows, int32_t max_context_len, int32_t k) {
+  return pmqa::select_workspace_bytes(rows, max_context_len, k);
+}
 
 pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
                           int32_t max_context_len, const int32_t* lengths, int32_t k,
@@ -502,7 +504,7 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
                 "logits_stride = %lld must be >= max_context_len and a multiple of 4",
                 (long long)logits_stride);
   pmqa_status_t st = check_topk_out(k, topk_indices, topk_values, topk_stride, rows,
-                                    select_workspace, select_workspace_bytes);
+                                    max_context_len, select_workspace, select_workspace_bytes);
   if (st != PMQA_OK) return st;
   int dev = 0;
   st = check_device(&dev);

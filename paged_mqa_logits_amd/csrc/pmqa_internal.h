@@ -71,11 +71,11 @@ hipError_t launch_append(int variant, const void* k, int32_t dtype, int64_t n,
 // lengths[r] columns (lengths given), else the fused indexer rule from
 // ctx / sched (batch, next_n, workers).  Writes out_idx [rows, ldk] and,
 // when not null, out_val [rows, ldk].  workspace: null, or at least
-// select_workspace_bytes(rows) bytes, 16-byte aligned (unused for more than
-// kSplitRows rows); with it, long rows are split over several workgroups.
+// select_workspace_bytes(rows, max_ctx, k) bytes, 16-byte aligned (unused
+// when that is 0); with it, long rows are split over several workgroups.
 // cus: compute units of the device.
 constexpr int32_t kSplitRows = 512;  // two rows per compute unit of an MI355X
-size_t select_workspace_bytes(int32_t rows);
+size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k);
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,

@@ -1002,8 +1002,8 @@ void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs
 
 }  // namespace
 
-size_t select_workspace_bytes(int32_t rows) {
-  if (rows < 1 || rows > kSplitRows) return 0;
+size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k) {
+  if (rows < 1 || rows > kSplitRows || max_ctx <= kStage || max_ctx <= k) return 0;
   const int64_t words = 3 * ws_words(rows) + ws_words((int64_t)rows * kMaxChunks) +
                         2 * ws_words((int64_t)rows * kRowSlots);
   return (size_t)words * 4;

@@ -144,20 +144,24 @@ def test_select_workspace_bytes():
 
     for rows in (1, 5, 100, 512):
         want = 4 * (3 * words(rows) + words(16 * rows) + 2 * words(6272 * rows))
-        assert pmqa.select_workspace_bytes(rows) == want, rows
-    assert pmqa.select_workspace_bytes(0) == 0
-    assert pmqa.select_workspace_bytes(513) == 0       # no split beyond 512 rows
+        assert pmqa.select_workspace_bytes(rows, 131072, 2048) == want, rows
+    assert pmqa.select_workspace_bytes(0, 131072, 2048) == 0
+    assert pmqa.select_workspace_bytes(513, 131072, 2048) == 0    # no split beyond 512 rows
+    assert pmqa.select_workspace_bytes(64, 7680, 16) == 0         # every row fits LDS
+    assert pmqa.select_workspace_bytes(64, 9000, 9000) == 0       # every row has <= k candidates
+    assert pmqa.select_workspace_bytes(64, 7681, 16) > 0
 
 
 def _select(lib, ws, ws_bytes, rows=4, k=8):
     p = ctypes.c_void_p
-    return lib.select_topk(p(FAKE), 256, rows, 256, p(FAKE), k, p(FAKE), p(FAKE), 8, p(ws),
+    return lib.select_topk(p(FAKE), 10000, rows, 10000, p(FAKE), k, p(FAKE), p(FAKE), 8, p(ws),
                            ws_bytes, p(0))
 
 
 def test_select_workspace_argument_checks():
     lib = pmqa.library()
-    need = pmqa.select_workspace_bytes(4)
+    need = pmqa.select_workspace_bytes(4, 10000, 8)
+    assert need > 0
     assert _select(lib, FAKE, need - 1) == 1
     assert "select_workspace_bytes" in pmqa.last_error()
     assert _select(lib, FAKE + 8, need) == 1

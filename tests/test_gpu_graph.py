@@ -90,7 +90,7 @@ def test_graph_replay_fused_topk_with_split_workspace():
     W = pmqa.default_num_workers()
     sched = torch.empty(pmqa.schedule_bytes(B, W) // 4, dtype=torch.int32, device="cuda")
     logits = torch.empty((B, M), dtype=torch.float32, device="cuda")
-    sws = torch.empty(pmqa.select_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    sws = torch.empty(pmqa.select_workspace_bytes(B, M, k), dtype=torch.uint8, device="cuda")
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     val = torch.empty((B, k), dtype=torch.float32, device="cuda")
 

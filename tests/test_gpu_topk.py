@@ -127,7 +127,7 @@ def test_select_topk_split_rows(k):
     n = np.array(lens + [131072, 131072], np.int32)
     buf = torch.from_numpy(x).cuda()
     lens_t = torch.from_numpy(n).cuda()
-    ws = torch.empty(pmqa.select_workspace_bytes(rows), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(pmqa.select_workspace_bytes(rows, M, k), dtype=torch.uint8, device="cuda")
     idx, val = pmqa.select_topk(buf, lens_t, k, select_workspace=ws)
     _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
     thr, cnt = _split_state(ws, rows)
@@ -162,7 +162,7 @@ def test_select_workspace_reused_across_calls():
     shorter lengths: nothing of the first call's lists leaks into it."""
     announce("select_topk workspace reuse")
     rng = np.random.default_rng(41)
-    ws = torch.empty(pmqa.select_workspace_bytes(12), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(pmqa.select_workspace_bytes(12, 100000, 2048), dtype=torch.uint8, device="cuda")
     k = 2048
     for rows, M in ((12, 100000), (5, 40000)):
         x = rng.standard_normal((rows, M)).astype(np.float32)
