@@ -17,8 +17,9 @@
 //      columns) builds a histogram of the keys' top 11 bits; the bin that
 //      holds the k-th largest key is b.
 //   2. A second pass gathers the keys of bin b with their columns (when
-//      there are at most 1024 of them, or 3840 for a row not copied to LDS,
-//      whose gather goes where the copy would be) and counts, per wavefront,
+//      there are at most 1024 of them, or 3840 -- 7680 with 1024 threads --
+//      for a row not copied to LDS, whose gather goes where the copy would
+//      be) and counts, per wavefront,
 //      the keys above bin b.  The remaining 21 bits of the k-th largest key
 //      K are found on the gathered list alone, which also gives each
 //      wavefront's count of keys above K and equal to K.  (A larger bin is
