@@ -438,8 +438,44 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
       prefix |= lds.chosen[0] << shift;
       pmask |= dmask << shift;
       krem -= lds.chosen[1];
+      const uint32_t h = lds.chosen[2];
       __syncthreads();
       top = shift;
+      if (top > 0 && h <= 64) {
+        // at most 64 keys share the prefix: one wavefront ranks them
+        uint32_t* small = lds.hist2;  // keys [0, 64), count at [64]
+        if (tid == 0) small[64] = 0;
+        __syncthreads();
+        for (uint32_t c = tid; c < limit; c += kSelThreads) {
+          const uint32_t key = ckey[c];
+          if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
+            small[atomicAdd(&small[64], 1u)] = key;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t cnt = small[64];
+          const uint32_t mine = lane < (int)cnt ? small[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t j = 0; j < cnt; ++j) {
+            const uint32_t o = small[j];
+            gt += o > mine ? 1u : 0u;
+            ge += o >= mine ? 1u : 0u;
+          }
+          const uint64_t m = __ballot(lane < (int)cnt && gt < krem && krem <= ge);
+          const int src = m ? __builtin_ctzll(m) : 0;
+          const uint32_t K = __shfl(mine, src, 64), g = __shfl(gt, src, 64);
+          if (lane == 0) {
+            lds.chosen[0] = K;
+            lds.chosen[1] = g;
+          }
+        }
+        __syncthreads();
+        prefix = lds.chosen[0];
+        pmask = ~0u;
+        krem -= lds.chosen[1];
+        __syncthreads();
+        top = 0;
+      }
     }
   };
 
