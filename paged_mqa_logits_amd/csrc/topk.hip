@@ -55,17 +55,17 @@
 //     each row not kept in LDS a key threshold from a sample of the row,
 //     chosen so that at least k keys reach it (but for a miss of several
 //     standard deviations) and about 1.4 k are expected to;
-//   * the gather reads every such row in chunks of 16384 columns or more,
-//     one workgroup per chunk, and lists the keys at or above the
-//     threshold, in column order, with their count per chunk.
+//   * the gather reads every such row in chunks of 16384 columns or more
+//     (a persistent grid takes the plan's list of chunks in turn, each
+//     workgroup requesting its next chunk's threshold while it reads the
+//     current one) and lists the keys at or above the threshold, in column
+//     order, with their count per chunk.
 // The selection then takes a split row's list (a few thousand keys) instead
 // of the row, resolves the k-th key on it and writes from it.  A list that
 // is not whole (a chunk with more keys than its slots) or holds fewer than k
 // keys (the sample missed) sends the row down the path above; either way the
 // result is the same.
 #include <hip/hip_runtime.h>
-
-#include <algorithm>
 
 #include "pmqa_internal.h"
 
@@ -150,6 +150,8 @@ __device__ __forceinline__ int32_t chunk_slot(int32_t c, int32_t j, int32_t n) {
 
 // The workspace of the split path, in sections of whole 256-byte blocks.
 struct SplitWs {
+  int32_t* hdr;    // [0]: chunks listed
+  int32_t* chunk;  // [rows * kMaxChunks]: (row << 4) | chunk, every chunk of every long row
   int32_t* map;    // [rows]: row taken by workgroup i of the selection
   int32_t* len;    // [rows]: candidates of each row
   uint32_t* thr;   // [rows]: key threshold of a split row, else kNoSplit
@@ -163,6 +165,10 @@ int64_t ws_words(int64_t n) { return (n + 63) & ~(int64_t)63; }
 SplitWs split_ws(void* base, int32_t rows) {
   int32_t* p = static_cast<int32_t*>(base);
   SplitWs w;
+  w.hdr = p;
+  p += 64;
+  w.chunk = p;
+  p += ws_words((int64_t)rows * kMaxChunks);
   w.map = p;
   p += ws_words(rows);
   w.len = p;
@@ -881,7 +887,8 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
 
 // The split path's plan, before the gather and the selection:
 //  * workgroup 0 orders the rows longest first (by count class, as
-//    row_of_rank; rows of one class in any order) into ws.map;
+//    row_of_rank; rows of one class in any order) into ws.map, and lists
+//    every chunk of every row not kept in LDS (ws.chunk, count in ws.hdr);
 //  * workgroup 1 + r sets row r's candidate count and, for a row not kept
 //    in LDS, the key threshold: from a sample of the row (512 of every 4096
 //    columns), the top 19 bits of the sampled key of rank
@@ -900,14 +907,21 @@ void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
   if (blockIdx.x == 0) {
     uint8_t* cls = reinterpret_cast<uint8_t*>(lds.stage);  // class of each row
     if (tid < kOrderBins) lds.hist[tid] = 0;
+    if (tid == 0) lds.chosen[2] = 0;
     __syncthreads();
     for (int32_t q = tid; q < rows; q += kSelThreads) {
-      const uint32_t c = count_class(
-          row_candidates(q, max_ctx, lengths, ctx, sched, batch, next_n, workers));
+      const int32_t n = row_candidates(q, max_ctx, lengths, ctx, sched, batch, next_n, workers);
+      const uint32_t c = count_class(n);
       cls[q] = (uint8_t)c;
       atomicAdd(&lds.hist[c], 1u);
+      if (n > k && n > kStage) {
+        const int32_t C = chunk_cols(n), nch = (n + C - 1) / C;
+        const uint32_t base = atomicAdd(&lds.chosen[2], (uint32_t)nch);
+        for (int32_t j = 0; j < nch; ++j) ws.chunk[base + j] = (q << 4) | j;
+      }
     }
     __syncthreads();
+    if (tid == 0) ws.hdr[0] = (int32_t)lds.chosen[2];
     if (tid < 64) {  // first rank of each class, from the top class down
       const int lane = tid;
       const uint32_t h0 = lds.hist[kOrderBins - 1 - 2 * lane];
@@ -973,6 +987,11 @@ void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
 // at or above the row's threshold goes, in column order, to the chunk's
 // slots of the row's list, and the count of those keys to ws.cnt (a count
 // above the chunk's slots marks the list as not whole).
+// Wave-uniform read through the constant address space (a scalar load).
+__device__ __forceinline__ int32_t sload(const int32_t* p) {
+  return __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(4))) int32_t*)(p));
+}
+
 template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs ws) {
@@ -980,68 +999,85 @@ void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs
   __shared__ SelLds<kSelThreads> lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // rows start at different chunks, so that the workgroups running at once
-  // do not all read the same columns of rows a power of two apart
-  const int32_t r = (int32_t)blockIdx.x;
-  const int32_t j = (int32_t)((blockIdx.y + blockIdx.x) % gridDim.y);
-  const uint32_t thr = ws.thr[r];
-  const int32_t n = ws.len[r];
-  if (thr == kNoSplit) return;
-  const int32_t C = chunk_cols(n), nch = (n + C - 1) / C;
-  if (j >= nch) return;
   const uint32_t R = (uint32_t)kListCap / kSelWaves;  // LDS list of each wavefront
   uint32_t* ckey = lds.cand_long.key;
   int32_t* ccol = lds.cand_long.col;
-  const int32_t s0 = j * C, s1 = min(n, s0 + C);
-  const int32_t lo = chunk_slot(s0, j, n), size = chunk_slot(s1, j + 1, n) - lo;
-  const int32_t L = ((s1 - s0 + kSelWaves - 1) / kSelWaves + 3) & ~3;
-  const int32_t c0 = min(s1, s0 + wave * L), c1 = min(s1, c0 + L);
-  const float* row = logits + (int64_t)r * ldo;
-  uint32_t mine = 0;
-  for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
-    uint64_t bc[4];
+  const int32_t total = sload(ws.hdr);
+  const int32_t G = (int32_t)gridDim.x;
+  int32_t c = (int32_t)blockIdx.x;
+  if (c >= total) return;
+  // the chunk in hand and the next one's list entry, one chunk ahead
+  int32_t e = sload(ws.chunk + c);
+  int32_t e_next = c + G < total ? sload(ws.chunk + c + G) : 0;
+  uint32_t thr = (uint32_t)sload(reinterpret_cast<const int32_t*>(ws.thr) + (e >> 4));
+  int32_t n = sload(ws.len + (e >> 4));
+  for (; c < total; c += G) {
+    const int32_t r = e >> 4, j = e & 15;
+    // request the next chunk's threshold and length, and the entry after it
+    const bool more = c + G < total;
+    const int32_t rn = e_next >> 4;
+    const uint32_t thr_n = more ? (uint32_t)sload(reinterpret_cast<const int32_t*>(ws.thr) + rn) : kNoSplit;
+    const int32_t n_n = more ? sload(ws.len + rn) : 0;
+    const int32_t e_nn = c + 2 * G < total ? sload(ws.chunk + c + 2 * G) : 0;
+    if (thr != kNoSplit) {
+      const int32_t C = chunk_cols(n);
+      const int32_t s0 = j * C, s1 = min(n, s0 + C);
+      const int32_t lo = chunk_slot(s0, j, n), size = chunk_slot(s1, j + 1, n) - lo;
+      const int32_t L = ((s1 - s0 + kSelWaves - 1) / kSelWaves + 3) & ~3;
+      const int32_t c0 = min(s1, s0 + wave * L), c1 = min(s1, c0 + L);
+      const float* row = logits + (int64_t)r * ldo;
+      uint32_t mine = 0;
+      for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
+        uint64_t bc[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bc[e] = __ballot(i + e < c1 && order_key(v[e]) >= thr);
-    uint32_t slot = mine;
+        for (int q = 0; q < 4; ++q) bc[q] = __ballot(i + q < c1 && order_key(v[q]) >= thr);
+        uint32_t slot = mine;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
+        for (int q = 0; q < 4; ++q) slot += lanes_below(bc[q]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (((bc[e] >> lane) & 1u) && slot < R) {
-        ckey[wave * R + slot] = order_key(v[e]);
-        ccol[wave * R + slot] = i + e;
+        for (int q = 0; q < 4; ++q) {
+          if (((bc[q] >> lane) & 1u) && slot < R) {
+            ckey[wave * R + slot] = order_key(v[q]);
+            ccol[wave * R + slot] = i + q;
+          }
+          slot += (bc[q] >> lane) & 1u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine += __builtin_popcountll(bc[q]);
+      });
+      if (lane == 0) lds.cand_cnt[wave] = mine;
+      __syncthreads();
+      uint32_t pos = 0, tot = 0;
+      bool over = false;
+      for (int w = 0; w < kSelWaves; ++w) {
+        const uint32_t m = lds.cand_cnt[w];
+        pos += w < wave ? m : 0u;
+        tot += m;
+        over = over || m > R;
       }
-      slot += (bc[e] >> lane) & 1u;
+      const uint32_t stored = min(mine, R);
+      const int64_t base = (int64_t)r * kRowSlots + lo;
+      for (uint32_t i = lane; i < stored; i += 64) {
+        if (pos + i < (uint32_t)size) {
+          ws.key[base + pos + i] = ckey[wave * R + i];
+          ws.col[base + pos + i] = ccol[wave * R + i];
+        }
+      }
+      if (tid == 0) ws.cnt[r * kMaxChunks + j] = over ? size + 1 : (int32_t)tot;
+      __syncthreads();  // the next chunk reuses the LDS lists
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
-  });
-  if (lane == 0) lds.cand_cnt[wave] = mine;
-  __syncthreads();
-  uint32_t pos = 0, total = 0;
-  bool over = false;
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t m = lds.cand_cnt[w];
-    pos += w < wave ? m : 0u;
-    total += m;
-    over = over || m > R;
+    e = e_next;
+    thr = thr_n;
+    n = n_n;
+    e_next = e_nn;
   }
-  const uint32_t stored = min(mine, R);
-  const int64_t base = (int64_t)r * kRowSlots + lo;
-  for (uint32_t i = lane; i < stored; i += 64) {
-    if (pos + i < (uint32_t)size) {
-      ws.key[base + pos + i] = ckey[wave * R + i];
-      ws.col[base + pos + i] = ccol[wave * R + i];
-    }
-  }
-  if (tid == 0) ws.cnt[r * kMaxChunks + j] = over ? size + 1 : (int32_t)total;
 }
 
 }  // namespace
 
 size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k) {
   if (rows < 1 || rows > kSplitRows || max_ctx <= kStage || max_ctx <= k) return 0;
-  const int64_t words = 3 * ws_words(rows) + ws_words((int64_t)rows * kMaxChunks) +
+  const int64_t words = 64 + 3 * ws_words(rows) + 2 * ws_words((int64_t)rows * kMaxChunks) +
                         2 * ws_words((int64_t)rows * kRowSlots);
   return (size_t)words * 4;
 }
@@ -1053,12 +1089,11 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k) {
 // 512 against 84 us with 1024.
 // With a workspace, at most kSplitRows rows (two per compute unit) and rows
 // that may be too long for LDS, the plan and gather kernels run first; the
-// gather has a workgroup for every chunk a row of max_ctx candidates could
-// have.  With more rows every
+// gather runs four workgroups per compute unit.  With more rows every
 // compute unit already holds several rows at once, and the single kernel is
 // faster (measured on MI355X: 2048 rows of up to 65536 columns select in
 // ~62 us alone against ~68 us split, 512 rows of up to 131072 in 92-113 us
-// alone against 61-67 us split).
+// alone against 59-64 us split).
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
@@ -1071,9 +1106,8 @@ hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, in
                        ldo, rows, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int32_t chunks = std::min<int32_t>(kMaxChunks, (max_ctx + kChunkMin - 1) / kChunkMin);
-    hipLaunchKernelGGL(select_gather_kernel<512>, dim3(rows, chunks), dim3(512), 0, stream,
-                       logits, ldo, ws);
+    hipLaunchKernelGGL(select_gather_kernel<512>, dim3(4 * (cus > 0 ? cus : 1)), dim3(512), 0,
+                       stream, logits, ldo, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -136,14 +136,15 @@ def test_binding_rejects_cpu_tensors():
 
 
 def test_select_workspace_bytes():
-    """Sections of whole 256-byte blocks: map, lengths and thresholds (one
-    word per row each), chunk counts (16 words per row), keys and columns
-    (6272 words per row each: 1.5 x 3840 list slots plus 32 per chunk)."""
+    """Sections of whole 256-byte blocks: a 64-word header, the chunk list
+    (16 words per row), map, lengths and thresholds (one word per row each),
+    chunk counts (16 words per row), keys and columns (6272 words per row
+    each: 1.5 x 3840 list slots plus 32 per chunk)."""
     def words(n):
         return (n + 63) // 64 * 64
 
     for rows in (1, 5, 100, 512):
-        want = 4 * (3 * words(rows) + words(16 * rows) + 2 * words(6272 * rows))
+        want = 4 * (64 + 3 * words(rows) + 2 * words(16 * rows) + 2 * words(6272 * rows))
         assert pmqa.select_workspace_bytes(rows, 131072, 2048) == want, rows
     assert pmqa.select_workspace_bytes(0, 131072, 2048) == 0
     assert pmqa.select_workspace_bytes(513, 131072, 2048) == 0    # no split beyond 512 rows

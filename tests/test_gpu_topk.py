@@ -149,12 +149,15 @@ def _chunk_cols(n):
 
 def _split_state(ws, rows):
     """Thresholds [rows] and chunk counts [rows, 16] the split path left in
-    its workspace (sections of whole 256-byte blocks: map, lengths,
-    thresholds, counts, keys, columns)."""
+    its workspace (sections of whole 256-byte blocks: header, chunk list,
+    map, lengths, thresholds, counts, keys, columns)."""
     w = ws.view(torch.int32).cpu().numpy()
     blk = -(-rows // 64) * 64
-    thr = w[2 * blk: 2 * blk + rows].view(np.uint32)
-    return thr, w[3 * blk: 3 * blk + 16 * rows].reshape(rows, 16)
+    c16 = -(-16 * rows // 64) * 64
+    t0 = 64 + c16 + 2 * blk
+    thr = w[t0: t0 + rows].view(np.uint32)
+    n0 = 64 + c16 + 3 * blk
+    return thr, w[n0: n0 + 16 * rows].reshape(rows, 16)
 
 
 def test_select_workspace_reused_across_calls():
