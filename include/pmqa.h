@@ -249,10 +249,9 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
  *   topk_stride     >= k.
  *   select_workspace        NULL, or a device buffer of at least
  *                   pmqa_select_workspace_bytes(rows, max_context_len, k)
- *                   bytes, 16-byte aligned,
- *                   owned by the caller, contents unspecified before and
- *                   after the call (error PMQA_ERR_INVALID_ARGUMENT when
- *                   smaller or misaligned).  With it, and at most 512 rows,
+ *                   bytes, 16-byte aligned, owned by the caller, contents
+ *                   unspecified before and after the call (error
+ *                   PMQA_ERR_INVALID_ARGUMENT when smaller or misaligned).  With it, and at most 512 rows,
  *                   the rows too long to be kept in LDS are split into
  *                   chunks over many workgroups (two more kernels run
  *                   first); the result is the same.  Calls that share one
