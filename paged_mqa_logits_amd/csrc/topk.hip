@@ -890,12 +890,13 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
 //    row_of_rank; rows of one class in any order) into ws.map, and lists
 //    every chunk of every row not kept in LDS (ws.chunk, count in ws.hdr);
 //  * workgroup 1 + r sets row r's candidate count and, for a row not kept
-//    in LDS, the key threshold: from a sample of the row (512 of every 4096
+//    in LDS, the key threshold: from a sample of the row (256 of every 4096
 //    columns), the top 19 bits of the sampled key of rank
-//    ks + 5 sqrt(ks) + 5, ks = k * (sample size) / n, so that at least k
-//    keys of the row reach it but for a five-sigma miss, and about
-//    (1 + 5 / sqrt(ks)) k are expected to.  A row whose expected list would
-//    not fit kListCap slots comfortably is not split.
+//    ks + 4.5 sqrt(ks) + 4.5, ks = k * (sample size) / n, so that at least
+//    k keys of the row reach it but for a 4.5-sigma miss, and about
+//    (1 + 4.5 / sqrt(ks)) k (1.4 k for k = 2048) are expected to.  A row
+//    whose expected list would not fit kListCap slots comfortably is not
+//    split.
 template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t rows,
@@ -982,15 +983,18 @@ void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
   }
 }
 
-// The split path's gather: workgroup (r, j) takes chunk j of row r (columns
-// [jC, min(n, (j+1)C))) when the row is split and has that chunk.  Every key
-// at or above the row's threshold goes, in column order, to the chunk's
-// slots of the row's list, and the count of those keys to ws.cnt (a count
-// above the chunk's slots marks the list as not whole).
 // Wave-uniform read through the constant address space (a scalar load).
 __device__ __forceinline__ int32_t sload(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(4))) int32_t*)(p));
 }
+
+// The split path's gather: a persistent grid takes the plan's chunk list in
+// turn; for chunk j of row r (columns [jC, min(n, (j+1)C))) of a split row,
+// every key at or above the row's threshold goes, in column order, to the
+// chunk's slots of the row's list, and the count of those keys to ws.cnt (a
+// count above the chunk's slots marks the list as not whole).  Each
+// workgroup requests its next chunk's threshold and length while it reads
+// the current chunk.
 
 template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
