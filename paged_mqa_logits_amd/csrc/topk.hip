@@ -1013,14 +1013,15 @@ void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs
   // the chunk in hand and the next one's list entry, one chunk ahead
   int32_t e = sload(ws.chunk + c);
   int32_t e_next = c + G < total ? sload(ws.chunk + c + G) : 0;
-  uint32_t thr = (uint32_t)sload(reinterpret_cast<const int32_t*>(ws.thr) + (e >> 4));
+  const int32_t* thr_w = reinterpret_cast<const int32_t*>(ws.thr);
+  uint32_t thr = (uint32_t)sload(thr_w + (e >> 4));
   int32_t n = sload(ws.len + (e >> 4));
   for (; c < total; c += G) {
     const int32_t r = e >> 4, j = e & 15;
     // request the next chunk's threshold and length, and the entry after it
     const bool more = c + G < total;
     const int32_t rn = e_next >> 4;
-    const uint32_t thr_n = more ? (uint32_t)sload(reinterpret_cast<const int32_t*>(ws.thr) + rn) : kNoSplit;
+    const uint32_t thr_n = more ? (uint32_t)sload(thr_w + rn) : kNoSplit;
     const int32_t n_n = more ? sload(ws.len + rn) : 0;
     const int32_t e_nn = c + 2 * G < total ? sload(ws.chunk + c + 2 * G) : 0;
     if (thr != kNoSplit) {
