@@ -245,6 +245,26 @@ def _sample_rows(d, k, seed):
 
 
 @pytest.mark.timeout(400)
+def test_million_token_row():
+    """A context of 2^20 tokens (4096 units, 16384 pages) next to a shorter
+    and an empty row, max_context_len 2^20: every element against the
+    oracle, and the fused top-k (k = 2048, the split path with 16 chunks of
+    65536 columns) against the same oracle logits."""
+    announce("2^20-token row")
+    M = 1 << 20
+    d = make_fp8(np.array([M, 70001, 0]), max_context_len=M, seed=77)
+    ref = oracle(d)
+    lg, _ = run(d)
+    parity.check(lg, ref, "2^20 row")
+    dev = upload(d)
+    sched = pmqa.compute_schedule(dev["context_lens"])
+    idx, val = pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                       dev["context_lens"], dev["block_table"], sched, M, 2048)
+    n = np.array([M, 70001, 0])
+    parity.check_topk(idx.cpu().numpy(), val.cpu().numpy(), ref, n, 2048, "2^20 row top-k")
+
+
+@pytest.mark.timeout(400)
 @pytest.mark.parametrize("name", ["large_fp8", "spec_fp8", "mxfp4", "large_fp8_h16"])
 def test_full_size_config_sampled(name):
     """Full configuration in the launch configuration the benchmark times
