@@ -245,22 +245,33 @@ def _sample_rows(d, k, seed):
 
 
 @pytest.mark.timeout(400)
-def test_million_token_row():
+@pytest.mark.parametrize("variant,next_n", [("fp8", 1), ("fp4", 1), ("fp8", 2)])
+def test_million_token_row(variant, next_n):
     """A context of 2^20 tokens (4096 units, 16384 pages) next to a shorter
     and an empty row, max_context_len 2^20: every element against the
     oracle, and the fused top-k (k = 2048, the split path with 16 chunks of
     65536 columns) against the same oracle logits."""
-    announce("2^20-token row")
+    announce(f"2^20-token row {variant} next_n={next_n}")
     M = 1 << 20
-    d = make_fp8(np.array([M, 70001, 0]), max_context_len=M, seed=77)
+    ctx = np.array([M, 70001, 0])
+    mk = make_fp8 if variant == "fp8" else make_fp4
+    d = mk(ctx, next_n=next_n, max_context_len=M, seed=77)
     ref = oracle(d)
     lg, _ = run(d)
     parity.check(lg, ref, "2^20 row")
     dev = upload(d)
-    sched = pmqa.compute_schedule(dev["context_lens"])
-    idx, val = pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
-                                       dev["context_lens"], dev["block_table"], sched, M, 2048)
-    n = np.array([M, 70001, 0])
+    vt = pmqa.VARIANT_FP8 if variant == "fp8" else pmqa.VARIANT_FP4
+    sched = pmqa.compute_schedule(dev["context_lens"], variant=vt, next_n=next_n)
+    if variant == "fp8":
+        idx, val = pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                           dev["context_lens"], dev["block_table"], sched, M,
+                                           2048)
+    else:
+        idx, val = pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"],
+                                           dev["weights"], dev["context_lens"],
+                                           dev["block_table"], sched, M, 2048)
+    # candidates of row b*next_n + j: its causal limit (every unit is scheduled)
+    n = np.clip(np.repeat(ctx, next_n) - next_n + 1 + np.tile(np.arange(next_n), len(ctx)), 0, M)
     parity.check_topk(idx.cpu().numpy(), val.cpu().numpy(), ref, n, 2048, "2^20 row top-k")
 
 
