@@ -15,6 +15,10 @@ module.  It shares none of its code:
 * all arithmetic is exact ``fractions.Fraction`` arithmetic, summed in plain
   Python loops.
 
+It also gives, for every scored entry, the exact magnitude sum
+``sum_h |w_h| * |scale_t * q_h . k_t|`` on which the per-entry parity bound
+of the reference rests (the bound is 2e-3 times it plus 1e-6).
+
 Cost is O(rows * tokens * H * D) Python operations: keep inputs tiny.
 """
 from fractions import Fraction
@@ -51,25 +55,30 @@ def _fp4_row_values(packed, scales, D) -> list:
     return vals
 
 
-def _score(row_q, k_vals, scale, w_row) -> Fraction:
+def _score(row_q, k_vals, scale, w_row):
+    """(logit, magnitude sum) of one entry, both exact."""
     total = Fraction(0)
+    mag = Fraction(0)
     for h, qh in enumerate(row_q):
         dot = Fraction(0)
         for a, b in zip(qh, k_vals):
             dot += a * b
         x = scale * dot
+        wh = Fraction(float(w_row[h]))
         if x > 0:
-            total += Fraction(float(w_row[h])) * x
-    return total
+            total += wh * x
+        mag += abs(wh) * abs(x)
+    return total, mag
 
 
 def _limit(ctx, next_n, j, M):
     return min(ctx - next_n + 1 + j, M)
 
 
-def logits_fp8(q, kv_cache, weights, context_lens, block_table, max_context_len,
-               page_size=64):
-    """Exact logits (list of lists; None marks a -inf entry) for the fp8 variant."""
+def entries_fp8(q, kv_cache, weights, context_lens, block_table, max_context_len,
+                page_size=64):
+    """Exact (logit, magnitude sum) pairs (list of lists; None marks a -inf
+    entry) for the fp8 variant."""
     B, NN, H, D = q.shape
     out = []
     for b in range(B):
@@ -93,9 +102,10 @@ def logits_fp8(q, kv_cache, weights, context_lens, block_table, max_context_len,
     return out
 
 
-def logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_table,
-               max_context_len, page_size=64):
-    """Exact logits (list of lists; None marks -inf) for the MXFP4 variant."""
+def entries_fp4(q, q_scale, kv_cache, weights, context_lens, block_table,
+                max_context_len, page_size=64):
+    """Exact (logit, magnitude sum) pairs (list of lists; None marks -inf)
+    for the MXFP4 variant."""
     B, NN, H, Dh = q.shape
     D = 2 * Dh
     nblk = D // 32
@@ -119,3 +129,27 @@ def logits_fp4(q, q_scale, kv_cache, weights, context_lens, block_table,
                 row.append(_score(qrow, kv, Fraction(1), weights[r]))
             out.append(row)
     return out
+
+
+def _part(rows, i):
+    return [[None if e is None else e[i] for e in row] for row in rows]
+
+
+def logits_fp8(*args, **kw):
+    """Exact logits (list of lists; None marks a -inf entry) for the fp8 variant."""
+    return _part(entries_fp8(*args, **kw), 0)
+
+
+def bounds_fp8(*args, **kw):
+    """Exact sum_h |w_h| |scale_t q_h . k_t| per scored entry (None where masked)."""
+    return _part(entries_fp8(*args, **kw), 1)
+
+
+def logits_fp4(*args, **kw):
+    """Exact logits (list of lists; None marks -inf) for the MXFP4 variant."""
+    return _part(entries_fp4(*args, **kw), 0)
+
+
+def bounds_fp4(*args, **kw):
+    """Exact sum_h |w_h| |q_h . k_t| per scored entry of the MXFP4 variant."""
+    return _part(entries_fp4(*args, **kw), 1)

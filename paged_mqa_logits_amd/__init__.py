@@ -159,6 +159,21 @@ def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None, num_heads=NU
     return int(out.value)
 
 
+def check_schedule_words(words, batch, num_workers):
+    """Raise ValueError unless a schedule tensor of `words` int32 words is
+    exactly the size for (batch, num_workers).  The logits and top-k wrappers
+    infer num_workers from a schedule's length, so every schedule buffer the
+    binding writes must have exactly that length: a larger one would be read
+    as a schedule for more workers, which the kernels then reject by
+    scoring nothing."""
+    need = schedule_bytes(batch, num_workers) // 4
+    if need == 0:
+        raise ValueError(f"invalid schedule size: batch {batch}, num_workers {num_workers}")
+    if words != need:
+        raise ValueError(f"schedule buffer has {words} words; batch {batch} with "
+                         f"{num_workers} workers needs exactly {need}")
+
+
 def _schedule_buffer(context_lens, num_workers, out, variant, next_n, num_heads=NUM_HEADS):
     _need(context_lens, "context_lens", (torch.int32,), ndim=1)
     B = context_lens.shape[0]
@@ -168,9 +183,8 @@ def _schedule_buffer(context_lens, num_workers, out, variant, next_n, num_heads=
     if out is None:
         out = torch.empty(words, dtype=torch.int32, device=context_lens.device)
     else:
-        _need(out, "out", (torch.int32,))
-        if out.numel() < words:
-            raise ValueError(f"schedule buffer has {out.numel()} words, needs {words}")
+        _need(out, "out", (torch.int32,), ndim=1)
+        check_schedule_words(out.numel(), B, W)
     return B, W, out
 
 
@@ -385,16 +399,22 @@ def paged_mqa_topk_fp4(q, q_scale, kv_cache, weights, context_lens, block_table,
     return indices[:, :k], None if values is None else values[:, :k]
 
 
-def _sched_workers(schedule, batch, num_workers):
-    """Worker count implied by the schedule's length (no device read)."""
+def sched_workers(words, batch, num_workers=None):
+    """Worker count of a schedule of `words` int32 words for `batch` rows (no
+    device read): `num_workers` when given, else the one count whose exact
+    schedule size is `words` (the binding writes schedules of exactly that
+    size, see check_schedule_words)."""
     if num_workers is not None:
         return int(num_workers)
-    words = schedule.numel()
     w2 = words - SCHED_HEADER - 2 - batch - 1        # = 2 * num_workers
     if w2 < 2 or w2 % 2:
         raise ValueError(f"schedule of {words} words does not fit batch {batch}; "
                          "pass num_workers explicitly")
     return w2 // 2
+
+
+def _sched_workers(schedule, batch, num_workers):
+    return sched_workers(schedule.numel(), batch, num_workers)
 
 
 DTYPE_F32 = 0

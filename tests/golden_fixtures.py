@@ -18,6 +18,11 @@ def _expected(vals):
     return np.array([-np.inf if v == "-inf" else float(v) for v in vals], dtype=np.float64)
 
 
+def _bound(vals):
+    """Hand-derived sum_h |w_h| |X_h| per entry; 0 where the entry is masked."""
+    return np.array([0.0 if v is None else float(v) for v in vals], dtype=np.float64)
+
+
 def load_fp8(case_index=0):
     with open(os.path.join(GOLDEN, "hand_fp8.json")) as f:
         fx = json.load(f)
@@ -44,7 +49,8 @@ def load_fp8(case_index=0):
     return {"q": qa, "kv_cache": kv, "weights": np.array(fx["weights"], np.float32),
             "context_lens": np.array(fx["context_lens"], np.int32), "block_table": bt,
             "max_context_len": fx["max_context_len"], "page_size": P, "next_n": fx["next_n"],
-            "expected": _expected(case["expected"])[None, :], "num_cases": len(fx["cases"])}
+            "expected": _expected(case["expected"])[None, :], "num_cases": len(fx["cases"]),
+            "bound": _bound(case["bound"])[None, :]}
 
 
 def load_fp4():
@@ -72,7 +78,8 @@ def load_fp4():
             "context_lens": np.array(fx["context_lens"], np.int32),
             "block_table": np.array(fx["block_table"], np.int32),
             "max_context_len": fx["max_context_len"], "page_size": P, "next_n": fx["next_n"],
-            "expected": _expected(fx["cases"][0]["expected"])[None, :]}
+            "expected": _expected(fx["cases"][0]["expected"])[None, :],
+            "bound": _bound(fx["cases"][0]["bound"])[None, :]}
 
 
 def _tokens_fp8(fx):
@@ -105,7 +112,7 @@ def embed_fp8(fx, H=64, D=128, P=64, num_pages=3, phys=1):
     bt[0, 0] = phys
     return {"q": q, "kv_cache": kv, "weights": w, "context_lens": fx["context_lens"].copy(),
             "block_table": bt, "max_context_len": M, "page_size": P, "next_n": 1,
-            "expected": fx["expected"]}
+            "expected": fx["expected"], "bound": fx["bound"]}
 
 
 def embed_fp4(fx, H=64, D=128, P=64, num_pages=3, phys=2):
@@ -135,4 +142,5 @@ def embed_fp4(fx, H=64, D=128, P=64, num_pages=3, phys=2):
     bt[0, 0] = phys
     return {"q": q, "q_scale": qs, "kv_cache": kv, "weights": w,
             "context_lens": fx["context_lens"].copy(), "block_table": bt,
-            "max_context_len": M, "page_size": P, "next_n": 1, "expected": fx["expected"]}
+            "max_context_len": M, "page_size": P, "next_n": 1, "expected": fx["expected"],
+            "bound": fx["bound"]}

@@ -40,6 +40,26 @@ def test_schedule_bytes():
     assert pmqa.schedule_bytes(3, 0) == 0
 
 
+def test_schedule_size_is_exact_in_the_binding():
+    """The binding's schedule buffers have exactly the size for their worker
+    count, so the worker count the logits wrappers infer from a length is
+    the one the schedule was built for."""
+    for B, W in [(4, 8), (4, 16), (2048, 1024), (1, 1)]:
+        words = pmqa.schedule_bytes(B, W) // 4
+        pmqa.check_schedule_words(words, B, W)
+        assert pmqa.sched_workers(words, B) == W
+        assert pmqa.sched_workers(words, B, num_workers=3) == 3
+    # a buffer sized for 16 workers offered for 8 is refused
+    with pytest.raises(ValueError, match="needs exactly"):
+        pmqa.check_schedule_words(pmqa.schedule_bytes(4, 16) // 4, 4, 8)
+    with pytest.raises(ValueError, match="needs exactly"):
+        pmqa.check_schedule_words(pmqa.schedule_bytes(4, 8) // 4 - 1, 4, 8)
+    with pytest.raises(ValueError, match="invalid schedule size"):
+        pmqa.check_schedule_words(10, 0, 8)
+    with pytest.raises(ValueError, match="does not fit"):
+        pmqa.sched_workers(pmqa.schedule_bytes(4, 8) // 4 + 1, 4)
+
+
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails first
 
 

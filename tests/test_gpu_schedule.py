@@ -1,5 +1,7 @@
 """GPU schedules (compute_schedule, compute_schedule_linear, refresh_schedule)
 against the oracle partition, exactly."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -124,6 +126,28 @@ def test_refresh_rebuilds_for_another_worker_count():
     big = torch.zeros(pmqa.schedule_bytes(4, 16) // 4, dtype=torch.int32, device="cuda")
     pmqa.compute_schedule(ctx, num_workers=16, out=big)
     assert _refresh(ctx, big, 16) == 0
-    pmqa.compute_schedule(ctx, num_workers=8, out=big)   # header now says W = 8
+    # the raw C entry point accepts a larger buffer; the binding does not
+    lib = pmqa.library()
+    st = lib.compute_schedule(ctypes.c_void_p(ctx.data_ptr()), 4, 8,
+                              ctypes.c_void_p(big.data_ptr()),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0                                   # header now says W = 8
     assert _refresh(ctx, big, 16) == 1
     assert np.array_equal(big.cpu().numpy(), _fresh(ctx, 16))
+
+
+def test_binding_refuses_a_schedule_buffer_of_another_size():
+    """A schedule buffer sized for 16 workers used for 8 would later be read
+    by the logits wrappers as a 16-worker schedule: the binding refuses it,
+    and the logits wrappers infer the worker count only from exact sizes."""
+    announce("schedule buffer size")
+    ctx = torch.tensor([700, 0, 3000, 12], dtype=torch.int32, device="cuda")
+    big = torch.zeros(pmqa.schedule_bytes(4, 16) // 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="needs exactly"):
+        pmqa.compute_schedule(ctx, num_workers=8, out=big)
+    with pytest.raises(ValueError, match="needs exactly"):
+        pmqa.refresh_schedule(ctx, big, num_workers=8)
+    with pytest.raises(ValueError, match="needs exactly"):
+        pmqa.compute_schedule_linear(ctx, num_workers=8, out=big)
+    s8 = pmqa.compute_schedule(ctx, num_workers=8)
+    assert pmqa.sched_workers(s8.numel(), 4) == 8

@@ -105,3 +105,96 @@ def test_hand_fixture_fp4():
     res = reference.paged_mqa_logits_fp4(e["q"], e["q_scale"], e["kv_cache"], e["weights"],
                                          e["context_lens"], e["block_table"], e["max_context_len"])
     assert np.array_equal(res["logits"].astype(np.float64), e["expected"])
+
+
+def _check_tol(tol, bounds, rel=1e-12):
+    """The oracle's per-entry bound against 2e-3 * (exact magnitude sum) + 1e-6."""
+    for i, row in enumerate(bounds):
+        for t, v in enumerate(row):
+            if v is None:
+                assert tol[i, t] == 0.0, (i, t)
+                continue
+            want = Fraction(2, 1000) * v + Fraction(1, 10 ** 6)
+            assert abs(Fraction(float(tol[i, t])) - want) <= Fraction(rel) * want, \
+                (i, t, float(tol[i, t]), float(want))
+
+
+@pytest.mark.parametrize("next_n", [1, 2])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_tol_matches_exact_bound(next_n, seed):
+    """The parity bound 2e-3 * sum_h |w_h| |scale_t q_h.k_t| + 1e-6 (the
+    stated tolerance) against the rational brute force's exact magnitude
+    sums, with negative token scales in one seed."""
+    ctx = [0, 5, 9] if next_n == 1 else [1, 7, 2]
+    d = make_fp8(ctx, next_n=next_n, max_context_len=10, seed=seed, num_heads=4,
+                 head_dim=16, page_size=4, negative_scales=(seed == 1))
+    res = reference.paged_mqa_logits_fp8(d["q"], d["kv_cache"], d["weights"], d["context_lens"],
+                                         d["block_table"], d["max_context_len"], page_size=4,
+                                         want_tol=True)
+    bounds = exact.bounds_fp8(d["q"], d["kv_cache"], d["weights"], d["context_lens"],
+                              d["block_table"], d["max_context_len"], page_size=4)
+    _check_tol(res["tol"], bounds)
+
+
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_fp4_tol_matches_exact_bound(next_n):
+    d = make_fp4([6, 0, 3], next_n=next_n, max_context_len=7, seed=3, num_heads=4,
+                 head_dim=64, page_size=4)
+    res = reference.paged_mqa_logits_fp4(d["q"], d["q_scale"], d["kv_cache"], d["weights"],
+                                         d["context_lens"], d["block_table"],
+                                         d["max_context_len"], page_size=4, want_tol=True)
+    bounds = exact.bounds_fp4(d["q"], d["q_scale"], d["kv_cache"], d["weights"],
+                              d["context_lens"], d["block_table"], d["max_context_len"],
+                              page_size=4)
+    _check_tol(res["tol"], bounds)
+
+
+def _check_tol_hand(tol, bound, expected):
+    """Hand-derived bounds: 2e-3 * bound + 1e-6 on scored entries, 0 on masked ones."""
+    masked = np.isneginf(expected)
+    assert np.all(tol[masked] == 0.0)
+    want = 2e-3 * bound[~masked] + 1e-6
+    assert np.allclose(tol[~masked], want, rtol=1e-12, atol=0.0), (tol, want)
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_hand_fixture_fp8_tol(case):
+    f = gf.load_fp8(case)
+    res = reference.paged_mqa_logits_fp8(f["q"], f["kv_cache"], f["weights"], f["context_lens"],
+                                         f["block_table"], f["max_context_len"],
+                                         page_size=f["page_size"], want_tol=True)
+    _check_tol_hand(res["tol"], f["bound"], f["expected"])
+    e = gf.embed_fp8(f)
+    res = reference.paged_mqa_logits_fp8(e["q"], e["kv_cache"], e["weights"], e["context_lens"],
+                                         e["block_table"], e["max_context_len"], want_tol=True)
+    _check_tol_hand(res["tol"], e["bound"], e["expected"])
+
+
+def test_hand_fixture_fp4_tol():
+    f = gf.load_fp4()
+    res = reference.paged_mqa_logits_fp4(f["q"], f["q_scale"], f["kv_cache"], f["weights"],
+                                         f["context_lens"], f["block_table"],
+                                         f["max_context_len"], page_size=f["page_size"],
+                                         want_tol=True)
+    _check_tol_hand(res["tol"], f["bound"], f["expected"])
+    e = gf.embed_fp4(f)
+    res = reference.paged_mqa_logits_fp4(e["q"], e["q_scale"], e["kv_cache"], e["weights"],
+                                         e["context_lens"], e["block_table"], e["max_context_len"],
+                                         want_tol=True)
+    _check_tol_hand(res["tol"], e["bound"], e["expected"])
+
+
+def test_exact_bound_is_the_magnitude_sum():
+    """On a fixture whose values are hand-derived, the brute force's exact
+    magnitude sums are the hand-derived bounds."""
+    for case in range(2):
+        f = gf.load_fp8(case)
+        b = exact.bounds_fp8(f["q"], f["kv_cache"], f["weights"], f["context_lens"],
+                             f["block_table"], f["max_context_len"], page_size=f["page_size"])
+        got = np.array([0.0 if v is None else float(v) for v in b[0]])
+        assert np.array_equal(got, f["bound"][0])
+    f = gf.load_fp4()
+    b = exact.bounds_fp4(f["q"], f["q_scale"], f["kv_cache"], f["weights"], f["context_lens"],
+                         f["block_table"], f["max_context_len"], page_size=f["page_size"])
+    got = np.array([0.0 if v is None else float(v) for v in b[0]])
+    assert np.array_equal(got, f["bound"][0])

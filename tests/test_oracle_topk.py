@@ -1,5 +1,6 @@
 """Pins of oracle/topk.py against brute force, a library sort and hand cases."""
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -7,13 +8,22 @@ import pytest
 from oracle import topk
 
 
+def _plain_key(x):
+    """Plain Python float order, with the one rule IEEE comparison lacks made
+    explicit: -0 < +0 (the pair compares the float first, and only two zeros
+    of opposite sign reach the second item)."""
+    x = float(x)
+    return (x, 1 if x == 0.0 and math.copysign(1.0, x) > 0 else 0)
+
+
 def _brute(values, n, k):
     """Best k-subset by exhaustive search: maximise the sorted values
-    lexicographically (largest first), prefer lower indices on equal values."""
+    lexicographically (largest first), prefer lower indices on equal values.
+    Independent of oracle/topk.py's bit-pattern keys."""
     row = list(np.asarray(values, np.float32)[:n])
     if n <= k:
         return list(range(n))
-    key = topk.order_key(np.array(row, np.float32)).tolist()
+    key = [_plain_key(v) for v in row]
     best = None
     for sub in itertools.combinations(range(n), k):
         score = (sorted((key[i] for i in sub), reverse=True), [-i for i in sorted(sub)])
@@ -73,3 +83,24 @@ def test_fused_row_length():
     assert topk.fused_row_length(1000, 1, 0, 700, 4) == 700      # truncated
     assert topk.fused_row_length(1000, 1, 0, 4096, 3) == 768     # schedule covers 3 units
     assert topk.fused_row_length(0, 2, 0, 4096, 0) == 0
+
+
+def test_order_key_against_plain_float_order_on_random_bit_patterns():
+    """The bit-pattern key against plain float comparison (with -0 < +0) on
+    20000 random fp32 bit patterns (NaN excluded) plus the special values:
+    sorted by key, consecutive values never decrease in the plain order, and
+    keys are equal exactly when the bit patterns are."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([-np.inf, np.inf, -0.0, 0.0, 1e-45, -1e-45, 1.0, -1.0],
+                       np.float32).view(np.uint32)
+    bits = np.concatenate([bits, special, special])
+    v = bits.view(np.float32)
+    v = v[~np.isnan(v)]
+    key = topk.order_key(v)
+    order = np.argsort(key, kind="stable")
+    sv, sk = v[order], key[order]
+    for a, b, ka, kb in zip(sv[:-1], sv[1:], sk[:-1], sk[1:]):
+        pa, pb = _plain_key(a), _plain_key(b)
+        assert pa <= pb
+        assert (ka == kb) == (pa == pb)
