@@ -23,8 +23,15 @@ Reported beside the step rate:
   decode_drift  a graph of [every non-empty row += 1 token, refresh_schedule,
                 logits call] replayed step after step: the schedule is rebuilt
                 on the device whenever a row crosses a 256-token boundary;
-  copy_gbps     a plain 1 GiB device-to-device copy on the same box, read +
-                written bytes per second (frac_of_copy = achieved / it);
+  ceiling       the practical HBM ceiling of the call on the same box: two
+                hand-written streaming kernels (libpmqa_ceiling.so) move
+                the call's bytes with no arithmetic, a gather that loads every
+                page the call reads (16-byte non-temporal buffer loads, in
+                the call's row order) and a non-temporal store sweep the size
+                of the output; each is swept over waves per SIMD (and pages in
+                flight) and the fastest shape kept.  copy_gbps = their bytes
+                over their summed time, frac_of_copy = achieved / copy_gbps;
+                torch_copy_gbps is a plain 1 GiB device copy, for reference;
   cpu_baseline  the fp64 CPU oracle on a fixed subset of the same rows.
 
 Workloads moving less than 512 MB per call (mid_fp8) would fit the 256 MB
@@ -219,6 +226,70 @@ def measure_append(pmqa, torch, batch, reps=20):
     return out
 
 
+def pages_read(ctx, block_table, max_ctx, page):
+    """Page ids the logits call reads, in row order: the first
+    ceil(min(ctx_b, max_ctx) / page) block-table entries of every row."""
+    n = (np.clip(ctx.astype(np.int64), 0, max_ctx) + page - 1) // page
+    mask = np.arange(block_table.shape[1])[None, :] < n[:, None]
+    return np.ascontiguousarray(block_table[mask].astype(np.int32))
+
+
+def measure_ceiling(torch, kv_cache, page_bytes, pages, out, reps=10):
+    """Streaming ceiling of one call's bytes: the fastest gather of `pages`
+    and the fastest non-temporal sweep over `out`, each timed with HIP events
+    on the current stream (mean per launch over `reps` back-to-back
+    launches)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_mqa_logits_amd", "libpmqa_ceiling.so"))
+    lib.pmqa_ceiling_gather.restype = ctypes.c_int
+    lib.pmqa_ceiling_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pmqa_ceiling_fill.restype = ctypes.c_int
+    lib.pmqa_ceiling_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    pg = torch.from_numpy(pages).cuda()
+    sink = torch.empty((8 * cus * 256 * 4,), dtype=torch.int32, device="cuda")
+
+    def per_launch_us(fn):
+        if fn() != 0:
+            raise RuntimeError("ceiling kernel launch refused its arguments")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    g_bytes = int(len(pages)) * page_bytes
+    gather = {}
+    for wps in (1, 2, 3, 4):
+        for fl in (2, 4):
+            us = per_launch_us(lambda: lib.pmqa_ceiling_gather(
+                ctypes.c_void_p(kv_cache.data_ptr()), kv_cache.shape[0], page_bytes,
+                ctypes.c_void_p(pg.data_ptr()), len(pages), cus * wps, fl,
+                ctypes.c_void_p(sink.data_ptr()), sp))
+            gather[f"{wps}w_{fl}p"] = round(g_bytes / (us * 1e-6) / 1e9, 1)
+    f_bytes = out.numel() * 4
+    fill = {}
+    for wps in (1, 2, 4, 8):
+        us = per_launch_us(lambda: lib.pmqa_ceiling_fill(
+            ctypes.c_void_p(out.data_ptr()), out.numel(), float("-inf"), cus * wps, sp))
+        fill[f"{wps}w"] = round(f_bytes / (us * 1e-6) / 1e9, 1)
+    g_best = max(gather, key=gather.get)
+    f_best = max(fill, key=fill.get)
+    t = g_bytes / (gather[g_best] * 1e9) + f_bytes / (fill[f_best] * 1e9)
+    del pg, sink
+    return {"gbps": (g_bytes + f_bytes) / t / 1e9, "us": round(t * 1e6, 1),
+            "gather_bytes": g_bytes, "fill_bytes": f_bytes,
+            "gather_gbps": gather, "gather_best": g_best,
+            "fill_gbps": fill, "fill_best": f_best}
+
+
 def describe(cfg):
     if cfg.ctx_kind == "lognormal":
         dist = (f"ctx lognormal(median {cfg.ctx_median:g}, sigma {cfg.ctx_sigma:g}) clipped "
@@ -331,17 +402,18 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     if scrub is None:
-        # back to back: the steady decode loop
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
+        # back to back: the steady decode loop, an event between replays
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
             graph.replay()
-        e1.record()
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms_step = e0.elapsed_time(e1) / args.steps
+        ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+        step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     else:
-        ms_step = float(timed(graph.replay, args.steps).mean())
+        step_ms = timed(graph.replay, args.steps)
+        ms_step = float(step_ms.mean())
     print(f"[bench] graph step {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     # the logits call alone (fill + unit kernel), events on the stream it is launched on
@@ -449,6 +521,13 @@ def main():
              "schedule_rebuilds": int(rebuilds.item())}
     del dgraph
 
+    # the practical ceiling: the call's page reads and output writes alone
+    ceiling = measure_ceiling(torch, dev["kv_cache"],
+                              pmqa.FP8_PAGE_BYTES if fp8 else pmqa.FP4_PAGE_BYTES,
+                              pages_read(ctx_np, data["block_table"], M, pmqa.PAGE_SIZE), out)
+    print(f"[bench] ceiling {ceiling['gbps']:.0f} GB/s ({ceiling['us']} us)", file=sys.stderr,
+          flush=True)
+
     # a plain device-to-device copy of 1 GiB on the same box (bytes read + written)
     src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -521,6 +600,9 @@ def main():
         "gbps": alg / (ms_step * 1e-3) / 1e9,
         "mall_scrub": scrub is not None,
         "algorithmic_bytes_per_step": alg,
+        "graph_step_us": {"mean": ms_step * 1e3, "median": float(np.median(step_ms)) * 1e3,
+                          "p10": float(np.percentile(step_ms, 10)) * 1e3,
+                          "p90": float(np.percentile(step_ms, 90)) * 1e3},
         "logits_call_us": {"mean": k_mean * 1e3, "median": float(np.median(k_ms)) * 1e3,
                              "p10": float(np.percentile(k_ms, 10)) * 1e3,
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
@@ -533,8 +615,10 @@ def main():
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
                                 f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
                      "kernel_source_hash": src_hash,
-                     "copy_gbps": copy_gbps,
-                     "frac_of_copy": achieved / copy_gbps if copy_gbps else None},
+                     "copy_gbps": ceiling["gbps"],
+                     "frac_of_copy": achieved / ceiling["gbps"],
+                     "torch_copy_gbps": copy_gbps},
+        "ceiling": ceiling,
         "mfma_busy_pct": read_mfma_busy(src_hash, args.workload),
         "sampled_parity": ok,
         "cpu_baseline": cpu,

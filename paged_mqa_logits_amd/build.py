@@ -1,4 +1,5 @@
-"""Build the HIP library ``libpmqa.so`` in-tree for gfx950.
+"""Build the HIP library ``libpmqa.so`` (and the measurement library
+``libpmqa_ceiling.so``) in-tree for gfx950.
 
 Usage: ``python paged_mqa_logits_amd/build.py`` (run as a script: importing the
 package would first load the library this builds).
@@ -15,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpmqa.so")
+# streaming ceiling kernels timed beside the logits call (bench.py only)
+CEILING_LIB = os.path.join(HERE, "libpmqa_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "schedule.hip", "logits_fp8.hip", "logits_fp4.hip", "tail_fill.hip",
@@ -45,19 +49,26 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    """Compile every source and link libpmqa.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every source and link libpmqa.so and libpmqa_ceiling.so;
+    returns the logits library's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

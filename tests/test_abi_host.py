@@ -13,8 +13,8 @@ pmqa = pytest.importorskip("paged_mqa_logits_amd",
                            reason="libpmqa.so not built (python paged_mqa_logits_amd/build.py)")
 
 
-def _declared_functions():
-    with open(HEADER) as f:
+def _declared_functions(header=HEADER):
+    with open(header) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([A-Za-z_][A-Za-z0-9_]*)\s*\(",
@@ -31,6 +31,27 @@ def test_library_exports_every_declared_symbol():
     lib = pmqa.library()
     for name in _declared_functions():
         assert hasattr(lib, name), name
+
+
+def test_ceiling_library_exports_its_header():
+    """The measurement library beside the logits library (streaming ceiling
+    kernels timed by bench.py) exports what include/pmqa_ceiling.h declares."""
+    names = _declared_functions(os.path.join(ROOT, "include", "pmqa_ceiling.h"))
+    assert names == ["pmqa_ceiling_fill", "pmqa_ceiling_gather"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_mqa_logits_amd", "libpmqa_ceiling.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+    # argument checks return 1 before any launch
+    p = ctypes.c_void_p
+    lib.pmqa_ceiling_gather.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_int32, p, p]
+    lib.pmqa_ceiling_fill.argtypes = [p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32, p]
+    fake = 0x10000
+    assert lib.pmqa_ceiling_gather(p(fake), 10, 8448, p(fake), 5, 4, 3, p(fake), p(0)) == 1
+    assert lib.pmqa_ceiling_gather(p(fake), 10, 4000, p(fake), 5, 4, 2, p(fake), p(0)) == 1
+    assert lib.pmqa_ceiling_gather(p(0), 10, 8448, p(fake), 5, 4, 2, p(fake), p(0)) == 1
+    assert lib.pmqa_ceiling_fill(p(fake), 6, 0.0, 4, p(0)) == 1
+    assert lib.pmqa_ceiling_fill(p(fake + 4), 8, 0.0, 4, p(0)) == 1
 
 
 def test_schedule_bytes():

@@ -59,3 +59,13 @@ def test_summary_readers_follow_the_hash(tmp_path, monkeypatch):
     assert bench.read_mfma_busy("abc", "large_fp8") == 15.5
     assert bench.read_mfma_busy("abc", "mxfp4") is None
     assert bench.read_mfma_busy("other", "large_fp8") is None
+
+
+def test_pages_read_by_hand():
+    """The ceiling gather's page list: the first ceil(min(ctx, M)/64) entries
+    of each row, in row order."""
+    bt = np.array([[7, 8, 9, 10], [3, 4, 5, 6], [1, 2, 11, 12]], np.int32)
+    ctx = np.array([65, 0, 300], np.int32)
+    got = bench.pages_read(ctx, bt, 200, 64)           # row 2 truncated to 200 -> 4 pages
+    assert got.tolist() == [7, 8, 1, 2, 11, 12]
+    assert got.dtype == np.int32 and got.flags["C_CONTIGUOUS"]

@@ -80,7 +80,8 @@ def test_graph_replay_fused_topk_with_split_workspace():
     """Capture schedule + fused top-k with the split workspace (plan, gather
     and selection kernels); lengths change in place between replays (rows
     long enough to be split, some crossing chunk boundaries).  Every replay
-    must equal an eager call on the same lengths, bit for bit."""
+    must equal an eager call on the same lengths, bit for bit, and be a
+    selection the fp64 oracle accepts for that step's lengths."""
     announce("graph replay fused top-k (split workspace)")
     B, M, k = 6, 40000, 2048
     ctx0 = np.array([9000, 0, 16300, 30000, 7000, 38000], np.int32)
@@ -126,6 +127,12 @@ def test_graph_replay_fused_topk_with_split_workspace():
         torch.cuda.synchronize()
         assert torch.equal(got_i, ei), it
         assert torch.equal(got_v.view(torch.int32), ev.view(torch.int32)), it
+        # against the oracle: every unit of a row is scheduled, so a row's
+        # candidates are its first min(ctx, M) columns
+        ref = oracle(dict(d, context_lens=ctx))
+        n = np.clip(ctx.astype(np.int64), 0, M)
+        parity.check_topk(got_i.cpu().numpy(), got_v.cpu().numpy(), ref, n, k,
+                          f"top-k replay {it}")
 
 
 def test_validate_mode_detects_stale_schedule(monkeypatch):

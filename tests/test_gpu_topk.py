@@ -267,17 +267,3 @@ def test_fused_topk_mismatched_schedule_selects_nothing():
     sched = pmqa.compute_schedule(dev["context_lens"], num_workers=16)
     idx, val = _fused(d, 8, dev=dev, num_workers=8, schedule=sched)
     assert np.all(idx == -1) and np.all(np.isneginf(val))
-
-
-@pytest.mark.timeout(400)
-def test_fused_topk_full_size_sampled():
-    announce("fused top-k large_fp8 k=2048 (sampled rows)")
-    d = make_workload("large_fp8")
-    idx, val = _fused(d, 2048)
-    ctx = d["context_lens"]
-    rng = np.random.default_rng(24)
-    rows = sorted(set(rng.choice(len(ctx), 6, replace=False).tolist()) |
-                  {int(np.argmax(ctx)), int(np.nonzero(ctx == 0)[0][0])})
-    ref = oracle(d, rows=rows)
-    n = _row_lengths(d, rows)
-    parity.check_topk(idx[rows], val[rows], ref, n, 2048, "large_fp8")
