@@ -314,6 +314,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload name (default: the B=2048 fp8 decode the metric is quoted on)")
+    ap.add_argument("--logits-only", action="store_true",
+                    help="time only the graph step and the logits call (for profiling runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this size "
                          "(reference kernel for rocprofv3 byte counters)")
@@ -432,113 +434,126 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
 
-    spare = torch.empty_like(sched)
-    ctx_dev = dev["context_lens"]
-    poke = lambda: spare[:1].fill_(0)
-    sched_us = {
-        "binary": per_call_us(lambda: pmqa.compute_schedule(ctx_dev, num_workers=W, out=spare)),
-        "linear": per_call_us(lambda: pmqa.compute_schedule_linear(ctx_dev, num_workers=W,
-                                                                   out=spare)),
-        "refresh_keep": per_call_us(lambda: pmqa.refresh_schedule(ctx_dev, spare, num_workers=W)),
-    }
-    sched_us["refresh_rebuild"] = per_call_us(
-        lambda: (poke(), pmqa.refresh_schedule(ctx_dev, spare, num_workers=W))) - per_call_us(poke)
+    def extras():
+        """Everything beside the graph step and the logits call: schedule
+        calls, appends, the top-k step, the decode-drift graph, the streaming
+        ceiling and a plain copy."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spare = torch.empty_like(sched)
+        ctx_dev = dev["context_lens"]
+        poke = lambda: spare[:1].fill_(0)
+        sched_us = {
+            "binary": per_call_us(lambda: pmqa.compute_schedule(ctx_dev, num_workers=W, out=spare)),
+            "linear": per_call_us(lambda: pmqa.compute_schedule_linear(ctx_dev, num_workers=W,
+                                                                       out=spare)),
+            "refresh_keep": per_call_us(lambda: pmqa.refresh_schedule(ctx_dev, spare, num_workers=W)),
+        }
+        sched_us["refresh_rebuild"] = per_call_us(
+            lambda: (poke(), pmqa.refresh_schedule(ctx_dev, spare, num_workers=W))) - per_call_us(poke)
 
-    append = measure_append(pmqa, torch, B)
+        append = measure_append(pmqa, torch, B)
 
-    # the indexer step: logits of the scheduled units, then the top k per row
-    # (no -inf fill), and the selection alone on this step's logits
-    K_TOP = 2048
-    ws = torch.empty_like(out)
-    tk_idx = torch.empty((B * NN, K_TOP), dtype=torch.int32, device="cuda")
-    tk_val = torch.empty((B * NN, K_TOP), dtype=torch.float32, device="cuda")
-    sel_bytes = pmqa.select_workspace_bytes(B * NN, M, K_TOP)
-    sel_ws = torch.empty(sel_bytes, dtype=torch.uint8, device="cuda") if sel_bytes else None
+        # the indexer step: logits of the scheduled units, then the top k per row
+        # (no -inf fill), and the selection alone on this step's logits
+        K_TOP = 2048
+        ws = torch.empty_like(out)
+        tk_idx = torch.empty((B * NN, K_TOP), dtype=torch.int32, device="cuda")
+        tk_val = torch.empty((B * NN, K_TOP), dtype=torch.float32, device="cuda")
+        sel_bytes = pmqa.select_workspace_bytes(B * NN, M, K_TOP)
+        sel_ws = torch.empty(sel_bytes, dtype=torch.uint8, device="cuda") if sel_bytes else None
 
-    def topk_call():
-        if fp8:
-            pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
-                                    dev["context_lens"], dev["block_table"], sched, M, K_TOP,
-                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
-                                    select_workspace=sel_ws)
-        else:
-            pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
-                                    dev["context_lens"], dev["block_table"], sched, M, K_TOP,
-                                    workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
-                                    select_workspace=sel_ws)
+        def topk_call():
+            if fp8:
+                pmqa.paged_mqa_topk_fp8(dev["q"], dev["kv_cache"], dev["weights"],
+                                        dev["context_lens"], dev["block_table"], sched, M, K_TOP,
+                                        workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
+                                        select_workspace=sel_ws)
+            else:
+                pmqa.paged_mqa_topk_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
+                                        dev["context_lens"], dev["block_table"], sched, M, K_TOP,
+                                        workspace=ws, indices=tk_idx, values=tk_val, num_workers=W,
+                                        select_workspace=sel_ws)
 
-    pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
-    lengths = torch.from_numpy(np.clip(ctx_np.astype(np.int64).repeat(NN) - NN + 1 +
-                                       np.tile(np.arange(NN), B), 0, M).astype(np.int32)).cuda()
-    topk = {"k": K_TOP,
-            "fused_call_us": round(per_call_us(topk_call, args.steps), 2),
-            "select_only_us": round(per_call_us(
-                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
-                                         select_workspace=sel_ws), args.steps), 2),
-            "select_single_kernel_us": round(per_call_us(
-                lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
-                                         select_workspace=None), args.steps), 2),
-            "select_workspace_mb": round(sel_bytes / 2**20, 1)}
+        pmqa.compute_schedule(dev["context_lens"], num_workers=W, out=sched)
+        lengths = torch.from_numpy(np.clip(ctx_np.astype(np.int64).repeat(NN) - NN + 1 +
+                                           np.tile(np.arange(NN), B), 0, M).astype(np.int32)).cuda()
+        topk = {"k": K_TOP,
+                "fused_call_us": round(per_call_us(topk_call, args.steps), 2),
+                "select_only_us": round(per_call_us(
+                    lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
+                                             select_workspace=sel_ws), args.steps), 2),
+                "select_single_kernel_us": round(per_call_us(
+                    lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
+                                             select_workspace=None), args.steps), 2),
+                "select_workspace_mb": round(sel_bytes / 2**20, 1)}
 
-    # decode drift: every non-empty row grows by one token per step, so rows
-    # cross 256-token boundaries as decoding goes on; the graph refreshes the
-    # schedule on the device (rebuilding it when a unit count changed) before
-    # the logits call
-    ctx_d = dev["context_lens"].clone()
-    grow = (ctx_d > 0).to(torch.int32)
-    sched_d = torch.empty_like(sched)
-    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    rebuilds = torch.zeros(1, dtype=torch.int32, device="cuda")
-    pmqa.compute_schedule(ctx_d, num_workers=W, out=sched_d)
+        # decode drift: every non-empty row grows by one token per step, so rows
+        # cross 256-token boundaries as decoding goes on; the graph refreshes the
+        # schedule on the device (rebuilding it when a unit count changed) before
+        # the logits call
+        ctx_d = dev["context_lens"].clone()
+        grow = (ctx_d > 0).to(torch.int32)
+        sched_d = torch.empty_like(sched)
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        rebuilds = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pmqa.compute_schedule(ctx_d, num_workers=W, out=sched_d)
 
-    def drift_step():
-        ctx_d.add_(grow)
-        pmqa.refresh_schedule(ctx_d, sched_d, num_workers=W, recomputed=flag)
-        if fp8:
-            pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], ctx_d,
-                                      dev["block_table"], sched_d, M, out=ws, num_workers=W)
-        else:
-            pmqa.paged_mqa_logits_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
-                                      ctx_d, dev["block_table"], sched_d, M, out=ws,
-                                      num_workers=W)
-        rebuilds.add_(flag)
+        def drift_step():
+            ctx_d.add_(grow)
+            pmqa.refresh_schedule(ctx_d, sched_d, num_workers=W, recomputed=flag)
+            if fp8:
+                pmqa.paged_mqa_logits_fp8(dev["q"], dev["kv_cache"], dev["weights"], ctx_d,
+                                          dev["block_table"], sched_d, M, out=ws, num_workers=W)
+            else:
+                pmqa.paged_mqa_logits_fp4(dev["q"], dev["q_scale"], dev["kv_cache"], dev["weights"],
+                                          ctx_d, dev["block_table"], sched_d, M, out=ws,
+                                          num_workers=W)
+            rebuilds.add_(flag)
 
-    torch.cuda.synchronize()
-    dgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(dgraph, stream=cap):
-            drift_step()
-    torch.cuda.current_stream().wait_stream(cap)
-    torch.cuda.synchronize()
-    rebuilds.zero_()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        dgraph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    drift = {"steps": args.steps, "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 1),
-             "schedule_rebuilds": int(rebuilds.item())}
-    del dgraph
+        torch.cuda.synchronize()
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(dgraph, stream=cap):
+                drift_step()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        rebuilds.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            dgraph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        drift = {"steps": args.steps, "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 1),
+                 "schedule_rebuilds": int(rebuilds.item())}
+        del dgraph
 
-    # the practical ceiling: the call's page reads and output writes alone
-    ceiling = measure_ceiling(torch, dev["kv_cache"],
-                              pmqa.FP8_PAGE_BYTES if fp8 else pmqa.FP4_PAGE_BYTES,
-                              pages_read(ctx_np, data["block_table"], M, pmqa.PAGE_SIZE), out)
-    print(f"[bench] ceiling {ceiling['gbps']:.0f} GB/s ({ceiling['us']} us)", file=sys.stderr,
-          flush=True)
+        # the practical ceiling: the call's page reads and output writes alone
+        # (the sweep writes the top-k workspace, an output-sized buffer: `out`
+        # keeps the last logits call's result for the parity check below)
+        ceiling = measure_ceiling(torch, dev["kv_cache"],
+                                  pmqa.FP8_PAGE_BYTES if fp8 else pmqa.FP4_PAGE_BYTES,
+                                  pages_read(ctx_np, data["block_table"], M, pmqa.PAGE_SIZE), ws)
+        print(f"[bench] ceiling {ceiling['gbps']:.0f} GB/s ({ceiling['us']} us)", file=sys.stderr,
+              flush=True)
 
-    # a plain device-to-device copy of 1 GiB on the same box (bytes read + written)
-    src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0.record(stream)
-    for _ in range(5):
+        # a plain device-to-device copy of 1 GiB on the same box (bytes read + written)
+        src = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
         dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
-    del src, dst
+        e0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+        del src, dst
+        return sched_us, append, topk, drift, ceiling, copy_gbps
+
+    if args.logits_only:
+        sched_us = append = topk = drift = ceiling = copy_gbps = None
+    else:
+        sched_us, append, topk, drift, ceiling, copy_gbps = extras()
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
@@ -607,7 +622,7 @@ def main():
                              "p10": float(np.percentile(k_ms, 10)) * 1e3,
                              "p90": float(np.percentile(k_ms, 90)) * 1e3},
         "decode_drift": drift,
-        "schedule_us": {k: round(v, 2) for k, v in sched_us.items()},
+        "schedule_us": {k: round(v, 2) for k, v in sched_us.items()} if sched_us else None,
         "append": append,
         "topk": topk,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -615,8 +630,8 @@ def main():
                      "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
                                 f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
                      "kernel_source_hash": src_hash,
-                     "copy_gbps": ceiling["gbps"],
-                     "frac_of_copy": achieved / ceiling["gbps"],
+                     "copy_gbps": ceiling["gbps"] if ceiling else None,
+                     "frac_of_copy": achieved / ceiling["gbps"] if ceiling else None,
                      "torch_copy_gbps": copy_gbps},
         "ceiling": ceiling,
         "mfma_busy_pct": read_mfma_busy(src_hash, args.workload),

@@ -81,6 +81,18 @@ typedef enum { PMQA_DTYPE_F32 = 0, PMQA_DTYPE_BF16 = 1 } pmqa_dtype_t;
  * thread. */
 const char* pmqa_last_error(void);
 
+/* Persistent-grid size W of the fp8 logits kernel with next_n 1 and 64 heads
+ * (the batch decode kernel) on `device`: compute units times its resident
+ * workgroups per compute unit times 4 wavefronts per workgroup (one worker =
+ * one wavefront).  Host-only query.  Returns -1 on failure (not a gfx950
+ * device, or a HIP error; pmqa_last_error() says which).
+ *
+ * Page: section 2 (a persistent grid whose work partition is computed per
+ * call).  Any W >= 1 gives bitwise-identical logits; W only sets how many
+ * workers share the units.  The other kernels' best W differs (MXFP4 runs
+ * two wavefronts per SIMD): pmqa_default_num_workers gives it per variant. */
+int pmqa_num_workers(int device);
+
 /* Persistent-grid size for a logits kernel on `device`: compute units times
  * the kernel's resident workgroups per compute unit times 4 wavefronts per
  * workgroup (one worker = one wavefront).  The kernel, and so its

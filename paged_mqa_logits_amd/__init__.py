@@ -22,6 +22,7 @@ Entry points (same names as the C ABI):
     paged_mqa_topk_fp4(q, q_scale, kv_cache, ..., k) -> (indices, values)
     quantize_append_fp8(k, slot_mapping, kv_cache) -> kv_cache
     quantize_append_fp4(k, slot_mapping, kv_cache) -> kv_cache
+    num_workers(device=None)
     default_num_workers(variant, next_n=1, device=None)
     schedule_bytes(batch, num_workers)
 """
@@ -49,7 +50,8 @@ STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_INVALID_ARGUMENT", 2: "PMQA_ERR_UNSUPPORTED
           3: "PMQA_ERR_INVALID_VALUE", 4: "PMQA_ERR_STALE_SCHEDULE",
           5: "PMQA_ERR_CAPTURING", 6: "PMQA_ERR_HIP"}
 
-EXPORTS = ("pmqa_last_error", "pmqa_default_num_workers", "pmqa_schedule_bytes",
+EXPORTS = ("pmqa_last_error", "pmqa_num_workers", "pmqa_default_num_workers",
+           "pmqa_schedule_bytes",
            "compute_schedule", "compute_schedule_linear", "refresh_schedule",
            "paged_mqa_logits_fp8", "paged_mqa_logits_fp4", "quantize_append_fp8",
            "quantize_append_fp4", "select_topk", "paged_mqa_topk_fp8", "paged_mqa_topk_fp4",
@@ -76,6 +78,8 @@ _lib.pmqa_last_error.restype = ctypes.c_char_p
 _lib.pmqa_last_error.argtypes = []
 _lib.pmqa_schedule_bytes.restype = ctypes.c_size_t
 _lib.pmqa_schedule_bytes.argtypes = [_i32, _i32]
+_lib.pmqa_num_workers.restype = ctypes.c_int
+_lib.pmqa_num_workers.argtypes = [ctypes.c_int]
 _lib.pmqa_default_num_workers.restype = ctypes.c_int
 _lib.pmqa_default_num_workers.argtypes = [ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_i32)]
 _lib.compute_schedule.restype = ctypes.c_int
@@ -149,6 +153,15 @@ _BYTE = (torch.uint8, torch.float8_e4m3fn, torch.int8)
 
 def schedule_bytes(batch, num_workers):
     return int(_lib.pmqa_schedule_bytes(int(batch), int(num_workers)))
+
+
+def num_workers(device=None):
+    """Persistent-grid size of the fp8 batch-decode kernel (next_n 1, 64 heads)."""
+    dev = torch.cuda.current_device() if device is None else int(device)
+    w = int(_lib.pmqa_num_workers(dev))
+    if w < 1:
+        raise RuntimeError(f"pmqa_num_workers({dev}) failed: {last_error()}")
+    return w
 
 
 def default_num_workers(variant=VARIANT_FP8, next_n=1, device=None, num_heads=NUM_HEADS):

@@ -277,6 +277,12 @@ pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next
   return ok();
 }
 
+int pmqa_num_workers(int device) {
+  int32_t w = 0;
+  if (pmqa_default_num_workers(device, PMQA_VARIANT_FP8, 1, 64, &w) != PMQA_OK) return -1;
+  return w;
+}
+
 namespace {
 
 pmqa_status_t check_schedule_args(const int32_t* context_lens, int32_t batch,

@@ -160,7 +160,7 @@ struct SplitWs {
   int32_t* col;    // [rows * kRowSlots]: their columns
 };
 
-int64_t ws_words(int64_t n) { return (n + 63) & ~(int64_t)63; }
+constexpr int64_t ws_words(int64_t n) { return (n + 63) & ~(int64_t)63; }
 
 SplitWs split_ws(void* base, int32_t rows) {
   int32_t* p = static_cast<int32_t*>(base);

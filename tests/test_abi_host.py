@@ -160,6 +160,14 @@ def test_refresh_schedule_flag_alignment():
     assert st == 1 and "recomputed" in pmqa.last_error()
 
 
+def test_num_workers_without_a_usable_device_returns_minus_one():
+    """pmqa_num_workers reports failure as -1 with a message (here: no GPU, or
+    none with the requested index)."""
+    lib = pmqa.library()
+    assert lib.pmqa_num_workers(1 << 20) == -1
+    assert pmqa.last_error() != ""
+
+
 def test_default_num_workers_argument_checks():
     lib = pmqa.library()
     out = ctypes.c_int32(0)

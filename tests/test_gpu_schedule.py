@@ -151,3 +151,15 @@ def test_binding_refuses_a_schedule_buffer_of_another_size():
         pmqa.compute_schedule_linear(ctx, num_workers=8, out=big)
     s8 = pmqa.compute_schedule(ctx, num_workers=8)
     assert pmqa.sched_workers(s8.numel(), 4) == 8
+
+
+def test_num_workers_is_the_fp8_decode_grid():
+    """pmqa_num_workers(device): the persistent grid of the fp8 batch-decode
+    kernel, the same count pmqa_default_num_workers gives for (fp8, next_n 1,
+    64 heads), a multiple of the compute units times 4 wavefronts."""
+    announce("pmqa_num_workers")
+    w = pmqa.num_workers()
+    assert w == pmqa.default_num_workers(pmqa.VARIANT_FP8, 1, num_heads=64)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert w % (4 * cus) == 0 and w >= 4 * cus
+    assert pmqa.library().pmqa_num_workers(torch.cuda.current_device()) == w
