@@ -280,6 +280,29 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
                           hipStream_t stream);
 
 /*
+ * select_topk_noalloc - select_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same selection, bit for bit, with the split
+ * workspace taken from a static scratch array of the library instead of a
+ * caller's buffer.  It allocates nothing: the array is part of the loaded
+ * code object, one copy per device (about 24.6 MiB, held until the process
+ * ends), enough for every call select_topk would split (at most 512 rows);
+ * a call needing more (not possible with the current sizes) returns
+ * PMQA_ERR_INVALID_ARGUMENT.
+ *
+ * Every call on a device shares that device's scratch, and the scratch keeps
+ * the last call's contents (no call depends on them).  Calls that may
+ * overlap on one device (different streams, or several host threads
+ * without ordering) race on it: order them on one stream.
+ *
+ * Arguments, results and errors as select_topk, without the workspace.
+ */
+pmqa_status_t select_topk_noalloc(const float* logits, int64_t logits_stride, int32_t rows,
+                                  int32_t max_context_len, const int32_t* lengths, int32_t k,
+                                  int32_t* topk_indices, float* topk_values,
+                                  int64_t topk_stride, hipStream_t stream);
+
+/*
  * pmqa_select_workspace_bytes - bytes of the optional select_workspace of
  * select_topk and paged_mqa_topk_fp8/fp4 for `rows` rows of at most
  * max_context_len candidates and this k (about 49 KB per row); 0 when no

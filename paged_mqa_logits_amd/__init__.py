@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
                          block_table, schedule, max_context_len, out=None)
     select_topk(logits, lengths, k) -> (indices, values)
     select_workspace_bytes(rows, max_context_len, k)
+    select_topk_noalloc(logits, lengths, k) -> (indices, values)
     paged_mqa_topk_fp8(q, kv_cache, weights, context_lens, block_table,
                        schedule, max_context_len, k) -> (indices, values)
     paged_mqa_topk_fp4(q, q_scale, kv_cache, ..., k) -> (indices, values)
@@ -55,7 +56,7 @@ EXPORTS = ("pmqa_last_error", "pmqa_num_workers", "pmqa_default_num_workers",
            "compute_schedule", "compute_schedule_linear", "refresh_schedule",
            "paged_mqa_logits_fp8", "paged_mqa_logits_fp4", "quantize_append_fp8",
            "quantize_append_fp4", "select_topk", "paged_mqa_topk_fp8", "paged_mqa_topk_fp4",
-           "pmqa_select_workspace_bytes")
+           "pmqa_select_workspace_bytes", "select_topk_noalloc")
 
 
 class PmqaError(RuntimeError):
@@ -93,6 +94,8 @@ _lib.paged_mqa_logits_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i
                                       _i64, _i32, _i32, _i64, _i32, _p]
 _lib.select_topk.restype = ctypes.c_int
 _lib.select_topk.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p, _sz, _p]
+_lib.select_topk_noalloc.restype = ctypes.c_int
+_lib.select_topk_noalloc.argtypes = [_p, _i64, _i32, _i32, _p, _i32, _p, _p, _i64, _p]
 _lib.pmqa_select_workspace_bytes.restype = _sz
 _lib.pmqa_select_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.paged_mqa_topk_fp8.restype = ctypes.c_int
@@ -370,6 +373,25 @@ def select_topk(logits, lengths, k, indices=None, values=None, want_values=True,
     _check(_lib.select_topk(_ptr(logits), logits.stride(0), rows, M, _ptr(lengths), int(k),
                             _ptr(indices), _ptr(values), ldk, _ptr(ws), ws_bytes,
                             _stream_ptr(stream)))
+    return indices[:, :k], None if values is None else values[:, :k]
+
+
+def select_topk_noalloc(logits, lengths, k, indices=None, values=None, want_values=True,
+                        stream=None):
+    """select_topk with the split workspace in the library's static scratch
+    (the C call allocates nothing; pass indices / values to allocate nothing
+    here either).  Calls overlapping on one device race on the scratch."""
+    _need(logits, "logits", (torch.float32,), ndim=2, contiguous=False)
+    _need(lengths, "lengths", (torch.int32,), ndim=1)
+    rows, M = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    if lengths.shape[0] != rows:
+        raise ValueError("lengths must have one entry per row")
+    indices, values, ldk = _topk_out(indices, values, rows, int(k), want_values, logits.device)
+    _check(_lib.select_topk_noalloc(_ptr(logits), logits.stride(0), rows, M, _ptr(lengths),
+                                    int(k), _ptr(indices), _ptr(values), ldk,
+                                    _stream_ptr(stream)))
     return indices[:, :k], None if values is None else values[:, :k]
 
 

@@ -523,6 +523,28 @@ pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t ro
   return ok();
 }
 
+pmqa_status_t select_topk_noalloc(const float* logits, int64_t logits_stride, int32_t rows,
+                                  int32_t max_context_len, const int32_t* lengths, int32_t k,
+                                  int32_t* topk_indices, float* topk_values,
+                                  int64_t topk_stride, hipStream_t stream) {
+  int dev = 0;
+  pmqa_status_t st = check_device(&dev);
+  if (st != PMQA_OK) return st;
+  void* scratch = nullptr;
+  const hipError_t e = pmqa::static_scratch(dev, &scratch);
+  if (e != hipSuccess)
+    return fail(PMQA_ERR_HIP, "static scratch of device %d: %s", dev, hipGetErrorString(e));
+  const size_t need = pmqa::select_workspace_bytes(rows, max_context_len, k);
+  const size_t have = pmqa::static_scratch_bytes();
+  if (need > have)
+    return fail(PMQA_ERR_INVALID_ARGUMENT,
+                "%d rows of %d candidates with k = %d need %zu bytes of scratch; the static "
+                "scratch holds %zu",
+                rows, max_context_len, k, need, have);
+  return select_topk(logits, logits_stride, rows, max_context_len, lengths, k, topk_indices,
+                     topk_values, topk_stride, scratch, have, stream);
+}
+
 pmqa_status_t paged_mqa_topk_fp8(const void* q, const void* kv_cache, const float* weights,
                                  const int32_t* context_lens, const int32_t* block_table,
                                  const int32_t* schedule, float* logits_workspace, int32_t k,

@@ -76,6 +76,12 @@ hipError_t launch_append(int variant, const void* k, int32_t dtype, int64_t n,
 // cus: compute units of the device.
 constexpr int32_t kSplitRows = 512;  // two rows per compute unit of an MI355X
 size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k);
+// The allocation-free selection's scratch: a static device array of
+// static_scratch_bytes() bytes (enough for select_workspace_bytes of any
+// call); static_scratch(dev, &p) gives device dev's copy, looked up once per
+// device.
+size_t static_scratch_bytes();
+hipError_t static_scratch(int dev, void** ptr);
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,

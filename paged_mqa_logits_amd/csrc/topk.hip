@@ -67,6 +67,9 @@
 // result is the same.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pmqa_internal.h"
 
 namespace pmqa {
@@ -1080,11 +1083,56 @@ void select_gather_kernel(const float* __restrict__ logits, int64_t ldo, SplitWs
 
 }  // namespace
 
+namespace {
+
+// Bytes of the split path's workspace for `rows` rows (any max_ctx and k).
+constexpr int64_t split_ws_bytes(int64_t rows) {
+  return 4 * (64 + 3 * ws_words(rows) + 2 * ws_words(rows * kMaxChunks) +
+              2 * ws_words(rows * kRowSlots));
+}
+
+// Scratch of the allocation-free selection (select_topk_noalloc): the split
+// workspace of the most rows that are ever split, ~24.6 MiB per device,
+// held until the process ends.  Host code never passes this name to a
+// kernel: it stands for the array only on the device; the address of each
+// device's copy comes from hipGetSymbolAddress below.
+constexpr int64_t kScratchBytes = split_ws_bytes(kSplitRows);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
 size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k) {
   if (rows < 1 || rows > kSplitRows || max_ctx <= kStage || max_ctx <= k) return 0;
-  const int64_t words = 64 + 3 * ws_words(rows) + 2 * ws_words((int64_t)rows * kMaxChunks) +
-                        2 * ws_words((int64_t)rows * kRowSlots);
-  return (size_t)words * 4;
+  return (size_t)split_ws_bytes(rows);
+}
+
+size_t static_scratch_bytes() { return (size_t)kScratchBytes; }
+
+hipError_t static_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+      // the address of this device's copy, looked up with the device current
+      int cur = 0;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev) hipSetDevice(cur);
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // Workgroups of 1024 threads when every row can have one at once (two per
