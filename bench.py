@@ -627,7 +627,7 @@ def main():
         "topk": topk,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": (f"paged_mqa_logits_{data['variant']} = neg_inf_fill_kernel + "
+                     "kernel": (f"paged_mqa_logits_{data['variant']} = {'neg_inf_fill_flat_kernel' if M % 4 == 0 else 'neg_inf_fill_kernel'} + "
                                 f"logits_kernel<{'Fp8' if fp8 else 'Fp4'}Format, {NN}, {H // 16}>"),
                      "kernel_source_hash": src_hash,
                      "copy_gbps": ceiling["gbps"] if ceiling else None,

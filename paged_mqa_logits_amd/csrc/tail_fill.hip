@@ -58,12 +58,27 @@ __global__ __launch_bounds__(kFillThreads) void neg_inf_fill_kernel(float* __res
   }
 }
 
+// The same sweep over a region whose rows are contiguous (ldo == max_ctx, a
+// multiple of 4): one flat range of quads, with no row arithmetic per store.
+__global__ __launch_bounds__(kFillThreads) void neg_inf_fill_flat_kernel(v4f* __restrict__ out,
+                                                                         int64_t quads) {
+  const float ninf = -__builtin_inff();
+  const v4f nv = {ninf, ninf, ninf, ninf};
+  const int64_t stride = (int64_t)gridDim.x * kFillThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kFillThreads + threadIdx.x; i < quads; i += stride)
+    __builtin_nontemporal_store(nv, out + i);
+}
+
 }  // namespace
 
 hipError_t launch_neg_inf_fill(float* out, int64_t ldo, int64_t rows, int32_t max_ctx,
                                int32_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(neg_inf_fill_kernel, dim3(blocks), dim3(kFillThreads), 0, stream, out, ldo,
-                     rows, max_ctx);
+  if (ldo == max_ctx && max_ctx % 4 == 0)
+    hipLaunchKernelGGL(neg_inf_fill_flat_kernel, dim3(blocks), dim3(kFillThreads), 0, stream,
+                       reinterpret_cast<v4f*>(out), rows * (int64_t)(max_ctx / 4));
+  else
+    hipLaunchKernelGGL(neg_inf_fill_kernel, dim3(blocks), dim3(kFillThreads), 0, stream, out,
+                       ldo, rows, max_ctx);
   return hipGetLastError();
 }
 
