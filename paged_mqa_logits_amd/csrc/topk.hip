@@ -9,62 +9,39 @@
 // ascending order with their values; a row with n < k writes all n and pads
 // with column -1, value -inf.
 //
-// One workgroup of 512 or 1024 threads per row; wavefront w owns the
-// contiguous chunk [w*L, (w+1)*L) of the row's columns in every pass, 4
-// columns per lane per 16-byte read.  Values are mapped to order-preserving
-// 32-bit keys.
-//   1. One read of the row (copied into LDS when it has at most 7680
-//      columns) builds a histogram of the keys' top 11 bits; the bin that
-//      holds the k-th largest key is b.
-//   2. A second pass gathers the keys of bin b with their columns (when
-//      there are at most 1024 of them, or 3840 -- 7680 with 1024 threads --
-//      for a row not copied to LDS, whose gather goes where the copy would
-//      be) and counts, per wavefront,
-//      the keys above bin b.  The remaining 21 bits of the k-th largest key
-//      K are found on the gathered list alone, which also gives each
-//      wavefront's count of keys above K and equal to K.  (A larger bin is
-//      resolved with further digit passes over the row and a counting pass
-//      instead.)
-//   3. A last pass writes the selected columns in order: keys above K, and
-//      the first ones (by column) equal to K; each wavefront starts at the
-//      output position the counts give it and ranks its columns with
-//      ballots.
-// A row not copied to LDS is sampled before step 1 (256 of every 4096
-// columns) to guess the bins near the k-th key; step 1 then also histograms
-// the next 8 bits of those bins, so when the guess holds, the k-th key's top
-// 19 bits are known after step 1, step 2 gathers every key at or above them
-// (the k - 1 above plus the few sharing them) in column order, and steps 2-3
-// run on that list without reading the row a third time.  A guess that
-// misses, or a list that would overflow a wavefront's share, takes the path
-// above.
-// Every pass reads 8 tiles ahead (8 16-byte reads in flight per lane for a
-// row in global memory; after the first pass they hit L2).
+// Values are mapped to order-preserving 32-bit keys where ties and signed
+// zeros matter; elsewhere they are compared and binned as floats.  Three
+// ways to select a row, each exact:
 //
-// Rows are taken longest first: a row's time grows with its candidate
-// count, and the dispatcher starts workgroups in index order, so workgroup i
-// selects for the row of rank i in decreasing candidate count (by a coarse
-// class: the top 3 bits of the count; ties by row index).  The longest rows
-// then start at once instead of whenever their index comes up.  Each
-// workgroup derives its row from the counts of all rows (for up to 8192
-// rows; beyond that workgroup i takes row i).
+//   * Rows of at most kWaveCols (4096) candidates: one wavefront per row,
+//     eight (512 threads) or sixteen (1024) rows to a workgroup, no
+//     workgroup barrier.  The wavefront reads its row three times (the
+//     first read from HBM, the others mostly from the caches): a histogram
+//     of value-linear bins set from a 64-point sample of the row, then the
+//     keys of the bin holding the k-th largest key (at most 64), whose
+//     ranking gives the cut (the k-th selected key and column), then the
+//     selected columns written in column order.  Rows of at most k
+//     candidates are copied.  A row the bins do not settle is selected by
+//     8-bit digits of its keys (four counting reads) instead.
+//   * Longer rows: one workgroup per row.  A 1/16 sample of the row gives a
+//     threshold T below which the k-th largest key lies only with a 4.5-sigma
+//     miss of the sample; one pass lists every key >= T (about 1.4 k) in LDS
+//     in column order, and the k-th largest listed key, the cut and the
+//     selection come from the list.  A list with fewer than k keys or one
+//     that overflows falls back to digit passes over the row (histograms of
+//     the keys' top 11 bits, then of further digits of the chosen bin).
+//   * With a workspace, at most 512 rows and rows longer than kSplitCols
+//     (524288) columns, each such row is split over workgroups first: a
+//     plan kernel orders the rows and sets each long row's key threshold
+//     from a sample, a gather kernel lists the keys at or above it chunk by
+//     chunk, and the selection works on the list (falling back as above when
+//     the list is not whole or too short).
 //
-// Split rows.  With a workspace and few rows (at most 512, two per compute
-// unit, so one workgroup per row would leave most of the chip waiting on the
-// longest rows), two kernels run before the selection:
-//   * the plan orders the rows once for all workgroups (ws.map) and gives
-//     each row not kept in LDS a key threshold from a sample of the row,
-//     chosen so that at least k keys reach it (but for a miss of several
-//     standard deviations) and about 1.4 k are expected to;
-//   * the gather reads every such row in chunks of 16384 columns or more
-//     (a persistent grid takes the plan's list of chunks in turn, each
-//     workgroup requesting its next chunk's threshold while it reads the
-//     current one) and lists the keys at or above the threshold, in column
-//     order, with their count per chunk.
-// The selection then takes a split row's list (a few thousand keys) instead
-// of the row, resolves the k-th key on it and writes from it.  A list that
-// is not whole (a chunk with more keys than its slots) or holds fewer than k
-// keys (the sample missed) sends the row down the path above; either way the
-// result is the same.
+// Measured on MI355X (2048 rows of lognormal lengths up to 65536, k = 2048):
+// the selection takes ~38 us, against ~59 us with one workgroup per row for
+// every row; the groups of wavefronts hold the short and middle rows with
+// little per-row overhead, while the long rows, a fifth of the rows but two
+// thirds of the columns, get a workgroup each.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -90,6 +67,7 @@ constexpr int kWin = 4;                  // first-digit bins given a second digi
 constexpr int kSampleRun = 256;          // a row not in LDS is sampled: the first 256
 constexpr int kSampleStride = 4096;      // columns of every 4096
 constexpr int kListCap = kCandLong;      // keys listed for a split row, at most
+constexpr int32_t kSplitCols = 65536 * 8;  // rows split with a workspace: longer than this
 constexpr int kMaxChunks = 16;           // chunks of a split row, at most
 constexpr int32_t kChunkMin = 16384;     // columns of a chunk, at least
 constexpr int kRowSlots = 3 * kListCap / 2 + 32 * kMaxChunks;  // list slots of a row
@@ -133,7 +111,6 @@ __device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
   return (int32_t)max((int64_t)0, min(min(lim, (int64_t)kUnit * c), (int64_t)max_ctx));
 }
 
-constexpr int kOrderRows = 8192;          // rows ordered longest first
 constexpr int kOrderBins = 128;           // count classes
 
 // Columns of each chunk of a split row of n candidates: at least kChunkMin,
@@ -319,96 +296,578 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return x;
 }
 
-// The row of rank `rank` in decreasing count class (ties: lower row first);
-// rows <= kOrderRows.  Every thread calls it; LDS is free on return.
-template <int kSelThreads, class Lds>
-__device__ __forceinline__ int32_t row_of_rank(Lds& lds, int32_t rank, int32_t rows,
-                                            int32_t max_ctx, const int32_t* lengths,
-                                            const int32_t* ctx, const int32_t* sched,
-                                            int32_t batch, int32_t next_n, int32_t workers) {
-  constexpr int kSelWaves = kSelThreads / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint8_t* cls = reinterpret_cast<uint8_t*>(lds.stage);  // class of each row
-  uint32_t* hist = lds.hist;
-  if (tid < kOrderBins) hist[tid] = 0;
-  __syncthreads();
-  for (int32_t q = tid; q < rows; q += kSelThreads) {
-    const uint32_t c =
-        count_class(row_candidates(q, max_ctx, lengths, ctx, sched, batch, next_n, workers));
-    cls[q] = (uint8_t)c;
-    atomicAdd(&hist[c], 1u);
-  }
-  __syncthreads();
-  // class holding the rank, counted from the top class down, and the rank
-  // of its first row
-  if (wave == 0) {
-    const uint32_t h0 = hist[kOrderBins - 1 - 2 * lane], h1 = hist[kOrderBins - 2 - 2 * lane];
-    const uint32_t own = h0 + h1;
-    uint32_t incl = own;
+// ---- value-linear bins and the listing path of a long row
+//
+// Values are binned linearly over a range [lo, hi]: bin(x) = clamp((x - lo)
+// s, 0, kFastBins - 1) truncated, s = kFastBins / (hi - lo).  Every step of
+// that map is monotone (a rounded subtraction and product, a clamp, a
+// truncation), so a key in a lower bin is never larger than a key in a
+// higher one, whatever the rounding; values outside [lo, hi] land in the end
+// bins.  Unlike bins of the keys' top bits, where most of a row's values
+// share the sign and exponent and crowd into a few bins, it spreads a row's
+// values over all bins.  Once the bin b of the k-th largest key is known,
+// its keys (at most 64) are listed in LDS and ranked, (key, column) against
+// (key, column); that gives the cut: the k-th selected key K and column C,
+// so that a column is selected exactly when its key is above K, or equal to
+// K at a column <= C.
+//
+// A long row's workgroup samples it (256 of every 4096 columns); the
+// sample's bins give a value T below which the k-th largest key lies only
+// with a 4.5-sigma miss of the sample, and about 1.4 k keys are expected at
+// or above it.  One pass lists every key >= T in LDS, in column order, each
+// wavefront in its own region; the k-th largest listed key is found with a
+// histogram of the list as above (its top bin bounded by the sample's
+// largest value), and the selection is written from the list.  A list with
+// fewer than k keys, a region that overflows or more than 64 keys in the
+// chosen bin sends the row to the digit passes, with the same result.
+constexpr int kFastBins = 1024;
+constexpr int kSmall = 64;     // keys of the k-th key's bin, at most
+constexpr int kListLoads = 8;  // 16-byte reads in flight per lane in the listing pass
+
+template <int kSelThreads>
+constexpr int fast_cap() { return kSelThreads >= 1024 ? 10240 : 5120; }
+
+template <int kSelThreads>
+struct FastLds {
+  static constexpr int kW = kSelThreads / 64;
+  uint32_t hist[kFastBins + 4];
+  uint32_t hist2[kFastBins + 4];
+  float key[fast_cap<kSelThreads>()];      // listed keys (their values), per-wavefront regions
+  uint16_t col[fast_cap<kSelThreads>()];   // their columns, from the wavefront's first
+  uint32_t skey[kSmall];                   // the keys of bin b ...
+  int32_t scol[kSmall];                    // ... and their columns
+  float wlo[kW], whi[kW];
+  uint32_t wcnt[kW];
+  uint32_t scnt;
+};
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// A wavefront's chunk [c0, c1) of a row as a buffer resource (whole quads:
+// a row's storage extends to a multiple of 4 columns); a read past it
+// returns zeros without touching memory.
+__device__ __forceinline__ rsrc_t chunk_rsrc(const float* row, int32_t c0, int32_t c1) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row + c0), 0,
+                                           ((c1 - c0 + 3) & ~3) * 4, 0x00020000);
+}
+
+// Columns t + 4 lane .. + 3 of a chunk (t from the chunk's first column), as
+// stored: the caller masks the columns past the chunk's end.
+__device__ __forceinline__ v4f rload(rsrc_t rs, int32_t t, int lane) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 4 * t, 0));
+}
+
+// Columns col..col+3 of a row of n candidates from global memory (the quad
+// read is clamped to the row's last quad), those at or past n as -inf.
+__device__ __forceinline__ v4f quad_at(const float* row, int32_t col, int32_t n) {
+  const float ninf = -__builtin_inff();
+  v4f v = *reinterpret_cast<const v4f*>(row + min(col, (n - 1) & ~3));
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    const uint32_t above = incl - own, rk = (uint32_t)rank;
-    if (above <= rk && rk < above + h0) {
-      lds.chosen[0] = kOrderBins - 1 - 2 * lane;
-      lds.chosen[1] = above;
-    } else if (above + h0 <= rk && rk < incl) {
-      lds.chosen[0] = kOrderBins - 2 - 2 * lane;
-      lds.chosen[1] = above + h0;
-    }
+  for (int e = 0; e < 4; ++e) v[e] = col + e < n ? v[e] : ninf;
+  return v;
+}
+
+// Calls f(column, values) for every quad of a long row's sample: the first
+// kSampleRun columns of every kSampleStride.
+template <int kSelThreads, class F>
+__device__ __forceinline__ void each_sample_quad(const float* row, int32_t n, F&& f) {
+  constexpr int32_t kRunQuads = kSampleRun / 4;
+  const int32_t groups = (n + kSampleStride - 1) / kSampleStride;
+  for (int32_t t = threadIdx.x; t < groups * kRunQuads; t += kSelThreads) {
+    const int32_t col = kSampleStride * (t / kRunQuads) + 4 * (t % kRunQuads);
+    if (col < n) f(col, quad_at(row, col, n));
   }
-  __syncthreads();
-  const uint32_t want_cls = lds.chosen[0], j = (uint32_t)rank - lds.chosen[1];
-  // the j-th row of that class in row order, 512 rows per round
-  uint32_t base = 0;
-  for (int32_t r0 = 0; r0 < rows; r0 += kSelThreads) {
-    const int32_t q = r0 + tid;
-    const bool in = q < rows && cls[q] == want_cls;
-    const uint64_t m = __ballot(in);
-    if (lane == 0) lds.wave_sum[wave] = __builtin_popcountll(m);
-    __syncthreads();
-    uint32_t before = base, total = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      before += w < wave ? lds.wave_sum[w] : 0u;
-      total += lds.wave_sum[w];
-    }
-    if (in && before + lanes_below(m) == j) lds.chosen[2] = (uint32_t)q;
-    base += total;
-    __syncthreads();
-    if (base > j) break;  // uniform
+}
+
+__device__ __forceinline__ uint32_t lin_bin(float x, float lo, float s) {
+  return (uint32_t)__builtin_amdgcn_fmed3f((x - lo) * s, 0.f, (float)(kFastBins - 1));
+}
+
+// Inclusive scan over the wavefront's 64 lanes with DPP: shifts within rows
+// of 16 lanes (row_shr 1, 2, 4, 8), then the last lane of row 0 into row 1
+// and of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31).  A lane without a source takes `id`.  No lane-address
+// registers are needed, unlike permute-based shuffles.
+template <class F>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, F op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+// Wavefront-wide minimum / maximum (uniform results).
+__device__ __forceinline__ float wave_min(float x) {
+  const uint32_t r = wave_scan(__float_as_uint(x), __float_as_uint(__builtin_inff()),
+                               [](uint32_t a, uint32_t b) {
+                                 return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+                               });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  const uint32_t r = wave_scan(__float_as_uint(x), __float_as_uint(-__builtin_inff()),
+                               [](uint32_t a, uint32_t b) {
+                                 return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                               });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
+}
+
+__device__ __forceinline__ uint32_t scan_add(uint32_t x) {
+  return wave_scan(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Inclusive scans within each row of 16 lanes (DPP row shifts).
+__device__ __forceinline__ uint32_t row16_scan_add(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
+  return x;
+}
+
+template <int NB = kFastBins>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t r, uint32_t& bin,
+                                         uint32_t& above, uint32_t& h) {
+  constexpr int kPer = NB / 64;
+  static_assert(kPer == 16 || kPer == 4, "16 or 4 bins per lane");
+  const int lane = threadIdx.x & 63;
+  const int base = NB - kPer * (lane + 1);
+  uint32_t own = 0;
+  const uint4* p = reinterpret_cast<const uint4*>(hist + base);
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const uint4 u = p[q];
+    own += u.x + u.y + u.z + u.w;
   }
-  const int32_t r = (int32_t)lds.chosen[2];
-  __syncthreads();
-  return r;
+  const uint32_t incl = scan_add(own);
+  const uint32_t excl = incl - own;
+  const uint64_t m = __ballot(excl < r && r <= incl);
+  const int src = m ? __builtin_ctzll(m) : 0;
+  const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+  const int jb = NB - kPer * src - 1 - (lane & (kPer - 1));  // lane j of a row: the j-th bin from the top
+  const uint32_t c = hist[jb];
+  const uint32_t ic = ex + row16_scan_add(c);
+  const uint64_t m2 = __ballot(lane < kPer && ic - c < r && r <= ic);
+  const int s2 = m2 ? __builtin_ctzll(m2) : 0;
+  bin = (uint32_t)__builtin_amdgcn_readlane(jb, s2);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)(ic - c), s2);
+  h = (uint32_t)__builtin_amdgcn_readlane((int)c, s2);
+}
+
+// The cut: the krem-th of the h keys of bin b (h <= kSmall, listed in LDS)
+// in the order (key descending, column ascending); every wavefront computes
+// it alone, lane j ranking key j against the others read lane by lane.  Also
+// returns how many of the bin's selected keys lie before column c0.
+__device__ __forceinline__ void find_cut(const uint32_t* skey, const int32_t* scol, uint32_t h,
+                                         uint32_t krem, int32_t c0, uint32_t& kc,
+                                         int32_t& cc, uint32_t& before) {
+  const int lane = threadIdx.x & 63;
+  const bool in = (uint32_t)lane < h;
+  const uint32_t kj = in ? skey[lane] : 0u;
+  const int32_t cj = in ? scol[lane] : 0;
+  uint32_t rank = 0;
+  for (uint32_t i = 0; i < h; ++i) {
+    const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, (int)i);
+    const int32_t ci = __builtin_amdgcn_readlane(cj, (int)i);
+    rank += ((ki > kj) | ((ki == kj) & (ci < cj))) ? 1u : 0u;
+  }
+  const uint64_t mc = __ballot(in & (rank + 1 == krem));
+  const int src = mc ? __builtin_ctzll(mc) : 0;
+  kc = (uint32_t)__builtin_amdgcn_readlane((int)kj, src);
+  cc = __builtin_amdgcn_readlane(cj, src);
+  before = (uint32_t)__builtin_popcountll(__ballot(in & (rank < krem) & (cj < c0)));
 }
 
 template <int kSelThreads>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t max_ctx,
-                        const int32_t* __restrict__ lengths, const int32_t* __restrict__ ctx,
-                        const int32_t* __restrict__ sched, int32_t batch, int32_t next_n,
-                        int32_t workers, int32_t k, int32_t* __restrict__ out_idx,
-                        float* __restrict__ out_val, int64_t ldk, SplitWs ws) {
-  constexpr int kSelWaves = kSelThreads / 64;
-  __shared__ SelLds<kSelThreads> lds;
+__device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* row, int32_t n,
+                                          int32_t k, int32_t* oi, float* ov) {
+  constexpr int W = kSelThreads / 64;
+  constexpr uint32_t R = (uint32_t)fast_cap<kSelThreads>() / W;  // entries of a region
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t rows = (int32_t)gridDim.x;
-  // with the split workspace, the plan kernel has ordered the rows and
-  // counted their candidates
-  const int64_t r = ws.map ? (int64_t)ws.map[blockIdx.x]
-                    : rows <= kOrderRows
-                        ? row_of_rank<kSelThreads>(lds, (int32_t)blockIdx.x, rows, max_ctx,
-                                                   lengths, ctx, sched, batch, next_n, workers)
-                        : (int64_t)blockIdx.x;
-  const float* row = logits + r * ldo;
-  int32_t* oi = out_idx + r * ldk;
-  float* ov = out_val ? out_val + r * ldk : nullptr;
-  const int32_t n = ws.map ? ws.len[r]
-                           : row_candidates((int32_t)r, max_ctx, lengths, ctx, sched, batch,
-                                            next_n, workers);
+  const int32_t L = ((n + W - 1) / W + 3) & ~3;
+  if (L > 65536) return false;  // column offsets are 16-bit; no LDS touched yet
+  const int32_t c0 = min(n, wave * L), c1 = min(n, c0 + L);
+  for (int j = tid; j <= kFastBins; j += kSelThreads) {
+    f.hist[j] = 0u;
+    f.hist2[j] = 0u;
+  }
+  if (tid == 0) f.scnt = 0u;
+  // 1. The sample's range, then its histogram.
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  each_sample_quad<kSelThreads>(row, n, [&](int32_t col, const v4f& x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (__builtin_isfinite(x[e])) {
+        lo = fminf(lo, x[e]);
+        hi = fmaxf(hi, x[e]);
+      }
+  });
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    f.wlo[wave] = lo;
+    f.whi[wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    lo = fminf(lo, f.wlo[w]);
+    hi = fmaxf(hi, f.whi[w]);
+  }
+  const float s = (float)kFastBins / (hi - lo);
+  if (!(hi > lo) || !(s > 0.f) || !__builtin_isfinite(s)) {
+    __syncthreads();
+    return false;
+  }
+  each_sample_quad<kSelThreads>(row, n, [&](int32_t col, const v4f& x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < n) atomicAdd(&f.hist[lin_bin(x[e], lo, s)], 1u);
+  });
+  __syncthreads();
+  // T: one bin below the sample key of rank ks + 4.5 sqrt(ks) + 4.5
+  const int32_t ns = sample_size<kSampleRun>(n);
+  const float ks = (float)k * (float)ns / (float)n;
+  const uint32_t rs = (uint32_t)min((float)ns, ceilf(ks + 4.5f * sqrtf(ks) + 4.5f));
+  uint32_t bs, a0, h0;
+  find_bin<>(f.hist, rs, bs, a0, h0);
+  const float T = lo + ((float)bs - 1.f) / s;
+  // 2. Every key >= T, in column order, into the wavefront's region: a
+  //    ring of kListLoads tiles in flight, each slot refilled (kListLoads
+  //    tiles ahead) as soon as it is used; reads past the chunk touch no
+  //    memory.
+  const rsrc_t rs_c = chunk_rsrc(row, c0, c1);
+  float* lkey = f.key + wave * R;
+  uint16_t* lcol = f.col + wave * R;
+  uint32_t mine = 0;
+  v4f x[kListLoads];
+#pragma unroll
+  for (int m = 0; m < kListLoads; ++m) x[m] = rload(rs_c, 256 * m, lane);
+  for (int32_t b0 = c0;; b0 += kListLoads * 256) {
+#pragma unroll
+    for (int m = 0; m < kListLoads; ++m) {
+      // columns of the lane at or past c1 (the chunk's end) are not the row's
+      const int32_t lim = c1 - (b0 + 256 * m + 4 * lane);
+      bool sel[4];
+      uint64_t ms[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sel[e] = (x[m][e] >= T) & (e < lim);
+        ms[e] = __ballot(sel[e]);
+      }
+      uint32_t slot = mine;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slot += lanes_below(ms[e]);
+      const uint32_t off = (uint32_t)(b0 + 256 * m + 4 * lane - c0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e] & (slot < R)) {
+          lkey[slot] = x[m][e];
+          lcol[slot] = (uint16_t)(off + e);
+        }
+        slot += sel[e] ? 1u : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine += (uint32_t)__builtin_popcountll(ms[e]);
+      x[m] = rload(rs_c, b0 - c0 + 256 * (m + kListLoads), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (b0 + kListLoads * 256 >= c1) break;  // one exit, at the end: every slot's wait is exact
+  }
+  if (lane == 0) f.wcnt[wave] = mine;
+  __syncthreads();
+  uint32_t total = 0;
+  bool over = false;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    total += f.wcnt[w];
+    over = over || f.wcnt[w] > R;
+  }
+  // 3. The k-th largest listed key: bins over [T, sample max].
+  const float s2 = hi > T ? (float)kFastBins / (hi - T) : 0.f;
+  if (over || total < (uint32_t)k || !(s2 > 0.f) || !__builtin_isfinite(s2)) {
+    __syncthreads();
+    return false;
+  }
+  for (uint32_t j = lane; j < mine; j += 64) atomicAdd(&f.hist2[lin_bin(lkey[j], T, s2)], 1u);
+  __syncthreads();
+  uint32_t b, above, h;
+  find_bin<>(f.hist2, (uint32_t)k, b, above, h);
+  if (h > kSmall) {
+    __syncthreads();
+    return false;
+  }
+  uint32_t gt = 0;
+  for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
+    const uint32_t j = j0 + lane;
+    const bool in = j < mine;
+    const float x = in ? lkey[j] : 0.f;
+    const uint32_t bn = lin_bin(x, T, s2);
+    gt += (uint32_t)__builtin_popcountll(__ballot(in & (bn > b)));
+    if (in & (bn == b)) {
+      const uint32_t slot = atomicAdd(&f.scnt, 1u);
+      if (slot < (uint32_t)kSmall) {
+        f.skey[slot] = order_key(x);
+        f.scol[slot] = c0 + (int32_t)lcol[j];
+      }
+    }
+  }
+  if (lane == 0) f.wcnt[wave] = gt;  // every wavefront read the counts above before the last barrier
+  __syncthreads();
+  uint32_t kc, pos;
+  int32_t cc;
+  find_cut(f.skey, f.scol, h, (uint32_t)k - above, c0, kc, cc, pos);
+#pragma unroll
+  for (int w = 0; w < W; ++w) pos += w < wave ? f.wcnt[w] : 0u;
+  // 4. The selection, from the wavefront's region in order.
+  for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
+    const uint32_t j = j0 + lane;
+    const bool in = j < mine;
+    const float x = in ? lkey[j] : 0.f;
+    const int32_t col = c0 + (in ? (int32_t)lcol[j] : 0);
+    const uint32_t key = order_key(x);
+    const bool sel = in & ((key > kc) | ((key == kc) & (col <= cc)));
+    const uint64_t m = __ballot(sel);
+    const uint32_t p = pos + lanes_below(m);
+    if (sel & (p < (uint32_t)k)) {
+      oi[p] = col;
+      if (ov) ov[p] = x;
+    }
+    pos += (uint32_t)__builtin_popcountll(m);
+  }
+  return true;
+}
+
+// ---- one wavefront per row
+//
+// A row of at most kWaveCols candidates is selected by one wavefront alone,
+// with no workgroup barrier: eight such rows share a workgroup (one per
+// wavefront), while longer rows get a workgroup each.  The wavefront reads
+// its row three times (the first read from HBM, the others mostly from the
+// caches), 256 columns per read instruction and kRing reads in flight:
+//   1. value-linear bins over the range of a 64-point sample of the row
+//      (values outside it land in the end bins), counted in the
+//      wavefront's own histogram;
+//   2. the keys of the bin b of the k-th largest key (at most 64) listed with
+//      their columns, and the cut found from them;
+//   3. the selected columns written in column order, each lane's rank
+//      within the wavefront from ballots.
+// A row whose sample has no finite range or whose bin b holds more than 64
+// keys is selected by 8-bit digits of its keys instead (four counting reads
+// and the write), the k-th key's equal keys taken by column.
+constexpr int32_t kWaveCols = 4096;  // rows selected by one wavefront, at most
+constexpr int kRing = 4;             // 16-byte reads in flight per lane
+
+struct WaveLds {
+  uint32_t hist[kFastBins + 4];  // [kFastBins]: columns out of range
+  uint32_t skey[kSmall];
+  int32_t scol[kSmall];
+};
+
+// Columns t + 4 lane .. + 3 of a row through its buffer resource (reads past
+// the row's storage return zeros without touching memory).
+__device__ __forceinline__ v4f row_quad(rsrc_t rs, int32_t t, int lane) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 4 * t, 0));
+}
+
+// Calls f(first column of the lane's quad, values) for every tile of 256
+// columns of the row in order, kRing reads in flight: each slot of the ring
+// is refilled kRing tiles ahead right after its tile is used, and the loop
+// has one exit, at its end, so every wait is for the slot's own read.
+template <class F>
+__device__ __forceinline__ void each_tile(rsrc_t rs, int32_t n, F&& f) {
+  const int lane = threadIdx.x & 63;
+  v4f x[kRing];
+#pragma unroll
+  for (int m = 0; m < kRing; ++m) x[m] = row_quad(rs, 256 * m, lane);
+  for (int32_t t0 = 0;; t0 += kRing * 256) {
+#pragma unroll
+    for (int m = 0; m < kRing; ++m) {
+      if (t0 + 256 * m < n) f(t0 + 256 * m + 4 * lane, x[m]);  // uniform
+      x[m] = row_quad(rs, t0 + 256 * (m + kRing), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t0 + kRing * 256 >= n) break;
+  }
+}
+
+// Writes the lane's selected columns of one quad (sel bit e: column i + e)
+// at their ranks: pos plus the selected columns of the lower lanes and of
+// the lane's own lower columns.  Returns the quad's selected count over the
+// wavefront.
+__device__ __forceinline__ uint32_t write_quad(const v4f& x, int32_t i, const bool (&sel)[4],
+                                               uint32_t pos, int32_t k, int32_t* oi, float* ov) {
+  uint64_t ms[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ms[e] = __ballot(sel[e]);
+  uint32_t p = pos;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p += lanes_below(ms[e]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (sel[e] & (p < (uint32_t)k)) {
+      oi[p] = i + e;
+      if (ov) ov[p] = x[e];
+    }
+    p += sel[e] ? 1u : 0u;
+  }
+  uint32_t tot = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) tot += (uint32_t)__builtin_popcountll(ms[e]);
+  return tot;
+}
+
+__device__ __forceinline__ bool wave_fast(WaveLds& w, const float* row, rsrc_t rs, int32_t n,
+                                          int32_t k, int32_t* oi, float* ov) {
+  const int lane = threadIdx.x & 63;
+  // the range of a sample of 64 columns spread over the row
+  const float sv = row[(int32_t)(((int64_t)lane * n) >> 6)];
+  for (int j = lane; j <= kFastBins; j += 64) w.hist[j] = 0u;
+  const float lo = wave_min(sv), hi = wave_max(sv);
+  const float s = (float)kFastBins / (hi - lo);
+  if (!(hi > lo) || !(s > 0.f) || !__builtin_isfinite(s)) return false;
+  // 1. the histogram (columns past n go to the extra bin)
+  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      atomicAdd(&w.hist[i + e < n ? lin_bin(x[e], lo, s) : (uint32_t)kFastBins], 1u);
+  });
+  uint32_t b, above, h;
+  find_bin<>(w.hist, (uint32_t)k, b, above, h);
+  if (h > kSmall) return false;
+  // 2. the keys of bin b, then the cut
+  uint32_t listed = 0;
+  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+    bool in[4];
+    uint64_t ms[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      in[e] = (i + e < n) & (lin_bin(x[e], lo, s) == b);
+      ms[e] = __ballot(in[e]);
+    }
+    uint32_t slot = listed;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) slot += lanes_below(ms[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (in[e] & (slot < (uint32_t)kSmall)) {
+        w.skey[slot] = order_key(x[e]);
+        w.scol[slot] = i + e;
+      }
+      slot += in[e] ? 1u : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) listed += (uint32_t)__builtin_popcountll(ms[e]);
+  });
+  uint32_t kc, unused;
+  int32_t cc;
+  find_cut(w.skey, w.scol, h, (uint32_t)k - above, 0, kc, cc, unused);
+  // 3. the selection
+  uint32_t pos = 0;
+  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+    bool sel[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = order_key(x[e]);
+      sel[e] = (i + e < n) & ((key > kc) | ((key == kc) & (i + e <= cc)));
+    }
+    pos += write_quad(x, i, sel, pos, k, oi, ov);
+  });
+  return true;
+}
+
+// The k-th largest key by 8-bit digits (four counting reads), then the
+// write: keys above it, and its equal keys in column order while they last.
+__device__ __forceinline__ void wave_radix(WaveLds& w, rsrc_t rs, int32_t n, int32_t k,
+                                           int32_t* oi, float* ov) {
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
+  for (int d = 24; d >= 0; d -= 8) {
+    const int lane = threadIdx.x & 63;
+    for (int j = lane; j < 256; j += 64) w.hist[j] = 0u;
+    each_tile(rs, n, [&](int32_t i, const v4f& x) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(x[e]);
+        if ((i + e < n) & ((key & pmask) == prefix)) atomicAdd(&w.hist[(key >> d) & 0xFFu], 1u);
+      }
+    });
+    uint32_t g, above, h;
+    find_bin<256>(w.hist, krem, g, above, h);
+    prefix |= g << d;
+    pmask |= 0xFFu << d;
+    krem -= above;
+  }
+  // prefix is the k-th largest key; krem of its equal keys are taken
+  uint32_t pos = 0, eq = 0;
+  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+    bool isq[4];
+    uint64_t mq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      isq[e] = (i + e < n) & (order_key(x[e]) == prefix);
+      mq[e] = __ballot(isq[e]);
+    }
+    uint32_t r = eq;  // equal keys before this lane's first column
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r += lanes_below(mq[e]);
+    bool sel[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = ((i + e < n) & (order_key(x[e]) > prefix)) | (isq[e] & (r < krem));
+      r += isq[e] ? 1u : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) eq += (uint32_t)__builtin_popcountll(mq[e]);
+    pos += write_quad(x, i, sel, pos, k, oi, ov);
+  });
+}
+
+// One row by one wavefront.
+__device__ __forceinline__ void select_row_wave(WaveLds& w, const float* row, int32_t n, int32_t k,
+                                                int32_t* oi, float* ov) {
+  const int lane = threadIdx.x & 63;
+  if (n <= k) {  // every candidate is selected: 4 columns per lane, 4 reads in flight
+    const float ninf = -__builtin_inff();
+    for (int32_t i0 = 4 * lane; i0 < k; i0 += 4 * 256) {
+      v4f x[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int32_t i = i0 + 256 * m;  // a quad of the row's storage when i < n
+        x[m] = i < n ? *reinterpret_cast<const v4f*>(row + i) : v4f{ninf, ninf, ninf, ninf};
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t c = i0 + 256 * m + e;
+          if (c < k) {
+            oi[c] = c < n ? c : -1;
+            if (ov) ov[c] = c < n ? x[m][e] : ninf;
+          }
+        }
+    }
+    return;
+  }
+  const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0,
+                                                      ((n + 3) & ~3) * 4, 0x00020000);
+  if (!wave_fast(w, row, rs, n, k, oi, ov)) wave_radix(w, rs, n, k, oi, ov);
+}
+
+// The selection of one row by the whole workgroup: a row of at most k
+// candidates is copied; a split row's list is used when whole; a row held in
+// registers or a longer row takes its fast path; anything else (or a fast
+// path that cannot settle the row) takes the digit passes.
+template <int kSelThreads>
+__device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<kSelThreads>& fast,
+                                              const float* row, int64_t r, int32_t n, int32_t k,
+                                              int32_t* oi, float* ov, SplitWs ws) {
+  constexpr int kSelWaves = kSelThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float ninf = -__builtin_inff();
 
   if (n <= k) {  // every candidate is selected
@@ -605,6 +1064,8 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
     }
     __syncthreads();  // the counts above are read before the path below reuses LDS
   }
+
+  if (fast_list<kSelThreads>(fast, row, n, k, oi, ov)) return;
 
   // 0. A row not kept in LDS is sampled first (256 contiguous columns of
   //    every 4096, so every read is a whole 1 KB line run): the first-digit
@@ -886,11 +1347,67 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t m
     pos += total;
     eq_rank += eq_total;
   });
+
+}
+
+// Workgroups [0, groups) are groups: wavefront w of group g selects row
+// g kSelWaves + w, unless the row has more than kWaveCols candidates.
+// Workgroup groups + r then selects row r, the whole workgroup on it, if it
+// has more than kWaveCols candidates, and exits at once otherwise; the
+// dispatcher refills the freed slots with the next workgroups, so the wide
+// rows start within a few microseconds.  With a split workspace the grid is
+// one workgroup per row instead, in the order the plan kernel set.
+template <int kSelThreads>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t rows,
+                        int32_t groups, int32_t max_ctx, const int32_t* __restrict__ lengths,
+                        const int32_t* __restrict__ ctx, const int32_t* __restrict__ sched,
+                        int32_t batch, int32_t next_n, int32_t workers, int32_t k,
+                        int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ldk,
+                        SplitWs ws) {
+  constexpr int W = kSelThreads / 64;
+  __shared__ union {
+    SelLds<kSelThreads> sel;
+    FastLds<kSelThreads> fast;
+    WaveLds wv[W];
+  } smem;
+  // 160 KB of LDS per compute unit: four workgroups of 512 threads or two
+  // of 1024 (eight wavefronts per SIMD)
+  static_assert(sizeof(smem) <= 160 * 1024 * kSelThreads / 2048, "LDS of a workgroup");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto cands = [&](int64_t q) {
+    return row_candidates((int32_t)q, max_ctx, lengths, ctx, sched, batch, next_n, workers);
+  };
+  if (ws.map) {
+    // the split path: the plan kernel has ordered the rows and counted
+    // their candidates
+    const int64_t r = ws.map[blockIdx.x];
+    select_row_wg<kSelThreads>(smem.sel, smem.fast, logits + r * ldo, r, ws.len[r], k,
+                               out_idx + r * ldk, out_val ? out_val + r * ldk : nullptr, ws);
+    return;
+  }
+  const int32_t g = (int32_t)blockIdx.x;
+  if (g < groups) {
+    const int64_t r = (int64_t)g * W + wave;
+    if (r >= rows) return;
+    const int32_t n = cands(r);
+    if (n > kWaveCols) return;  // a wide worker's
+    select_row_wave(smem.wv[wave], logits + r * ldo, n, k, out_idx + r * ldk,
+                    out_val ? out_val + r * ldk : nullptr);
+    return;
+  }
+  const int64_t r = g - groups;
+  const int32_t n = cands(r);
+  if (n <= kWaveCols) return;  // a group's
+  select_row_wg<kSelThreads>(smem.sel, smem.fast, logits + r * ldo, r, n, k, out_idx + r * ldk,
+                             out_val ? out_val + r * ldk : nullptr, SplitWs{});
 }
 
 // The split path's plan, before the gather and the selection:
-//  * workgroup 0 orders the rows longest first (by count class, as
-//    row_of_rank; rows of one class in any order) into ws.map, and lists
+//  * workgroup 0 orders the rows longest first (by count class: 0 for none,
+//    else 1 + 4 floor(log2 n) + the two bits below the leading one; rows of
+//    one class in any order) into ws.map, and lists
 //    every chunk of every row not kept in LDS (ws.chunk, count in ws.hdr);
 //  * workgroup 1 + r sets row r's candidate count and, for a row not kept
 //    in LDS, the key threshold: from a sample of the row (256 of every 4096
@@ -1106,7 +1623,7 @@ std::mutex g_scratch_mu;
 }  // namespace
 
 size_t select_workspace_bytes(int32_t rows, int32_t max_ctx, int32_t k) {
-  if (rows < 1 || rows > kSplitRows || max_ctx <= kStage || max_ctx <= k) return 0;
+  if (rows < 1 || rows > kSplitRows || max_ctx <= kSplitCols || max_ctx <= k) return 0;
   return (size_t)split_ws_bytes(rows);
 }
 
@@ -1136,24 +1653,19 @@ hipError_t static_scratch(int dev, void** ptr) {
 }
 
 // Workgroups of 1024 threads when every row can have one at once (two per
-// compute unit), else of 512 (four per compute unit): measured on MI355X,
-// 512 rows of up to 131072 columns select in 90-110 us with 1024 threads
-// against 104-130 us with 512, and 2048 rows of up to 65536 in 64 us with
-// 512 against 84 us with 1024.
-// With a workspace, at most kSplitRows rows (two per compute unit) and rows
-// that may be too long for LDS, the plan and gather kernels run first; the
-// gather runs four workgroups per compute unit.  With more rows every
-// compute unit already holds several rows at once, and the single kernel is
-// faster (measured on MI355X: 2048 rows of up to 65536 columns select in
-// ~62 us alone against ~68 us split, 512 rows of up to 131072 in 92-113 us
-// alone against 59-64 us split).
+// compute unit), else of 512 (four per compute unit).  Measured on MI355X:
+// 512 rows of up to 131072 columns (nearly all of them long) select in
+// ~52-63 us with 1024 threads; 2048 rows of lognormal lengths up to 65536 in
+// ~38 us with 512.  With a workspace, at most kSplitRows rows and rows that
+// may be longer than kSplitCols (more than the listing path's 16-bit column
+// offsets reach with 512 threads), the plan and gather kernels run first.
 hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, int32_t max_ctx,
                               const int32_t* lengths, const int32_t* ctx, const int32_t* sched,
                               int32_t batch, int32_t next_n, int32_t workers, int32_t k,
                               int32_t* out_idx, float* out_val, int64_t ldk, void* workspace,
                               int32_t cus, hipStream_t stream) {
   SplitWs ws = {};
-  if (workspace && rows <= kSplitRows && max_ctx > kStage && max_ctx > k) {
+  if (workspace && rows <= kSplitRows && max_ctx > kSplitCols && max_ctx > k) {
     ws = split_ws(workspace, rows);
     hipLaunchKernelGGL(select_plan_kernel<512>, dim3(rows + 1), dim3(512), 0, stream, logits,
                        ldo, rows, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, ws);
@@ -1164,14 +1676,21 @@ hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, in
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((int64_t)rows <= 2 * (int64_t)cus)
-    hipLaunchKernelGGL(select_topk_kernel<1024>, dim3(rows), dim3(1024), 0, stream, logits, ldo,
-                       max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
-                       ldk, ws);
+  const int64_t c = cus > 0 ? cus : 1;
+  const bool big = (int64_t)rows <= 2 * c;  // 1024 threads: two workgroups per compute unit
+  const int32_t waves = big ? 16 : 8;
+  // without a split workspace: groups of wavefronts, then one workgroup per
+  // row for the wide rows
+  const int32_t groups = ws.map ? 0 : (int32_t)(((int64_t)rows + waves - 1) / waves);
+  const dim3 grid(ws.map ? rows : groups + rows);
+  if (big)
+    hipLaunchKernelGGL(select_topk_kernel<1024>, grid, dim3(1024), 0, stream, logits, ldo, rows,
+                       groups, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
+                       out_val, ldk, ws);
   else
-    hipLaunchKernelGGL(select_topk_kernel<512>, dim3(rows), dim3(512), 0, stream, logits, ldo,
-                       max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx, out_val,
-                       ldk, ws);
+    hipLaunchKernelGGL(select_topk_kernel<512>, grid, dim3(512), 0, stream, logits, ldo, rows,
+                       groups, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
+                       out_val, ldk, ws);
   return hipGetLastError();
 }
 

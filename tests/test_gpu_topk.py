@@ -21,8 +21,8 @@ def _rows(rng, rows, M, pool):
     return (rng.standard_normal((rows, M)) * 10).astype(np.float32)
 
 
-# "auto": the binding passes a workspace (rows ordered by the plan kernel,
-# long rows split over workgroups); None: the single-kernel path.
+# "auto": the binding passes a workspace when rows are long enough to be
+# split (more than 524288 columns, at most 512 rows); None: never split.
 WS = ["auto", None]
 
 
@@ -55,9 +55,10 @@ def test_select_topk_matches_oracle(pool, M, stride, k, ws):
 @pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("rows", [512, 513, 3000, 8192, 8193])
 def test_select_topk_many_rows(rows, ws):
-    """Workgroups take rows longest first (by count class) up to 8192 rows,
-    in index order beyond: every row is still selected exactly once, with
-    lengths spread over many classes and many rows per class."""
+    """Rows of at most 4096 candidates are selected by one wavefront each,
+    eight (or sixteen) to a workgroup: every row is selected exactly once
+    however the rows fall into the groups, with many empty and equal
+    lengths."""
     announce(f"select_topk rows={rows} ws={ws}")
     rng = np.random.default_rng(rows)
     M, k = 300, 17
@@ -71,13 +72,33 @@ def test_select_topk_many_rows(rows, ws):
 
 
 @pytest.mark.parametrize("ws", WS)
+def test_select_topk_many_wide_rows(ws):
+    """More rows than workgroups resident at once, most of them longer than
+    a wavefront takes (one workgroup each, started as the short rows' slots
+    free up), beside rows a wavefront takes and rows of at most k
+    candidates."""
+    announce(f"select_topk 1500 rows of up to 12000 ws={ws}")
+    rng = np.random.default_rng(77)
+    rows, M, k = 1500, 12000, 2048
+    x = rng.standard_normal((rows, M)).astype(np.float32)
+    n = rng.integers(4097, M + 1, size=rows).astype(np.int32)
+    n[::5] = rng.integers(2049, 4097, size=len(n[::5]))
+    n[::7] = rng.integers(0, 2049, size=len(n[::7]))
+    n[3::11] = 4096
+    n[4::11] = 4097
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+
+
+@pytest.mark.parametrize("ws", WS)
 def test_select_topk_long_rows_sample_misses_and_overflows(ws):
-    """Rows too long for LDS are sampled (256 of every 4096 columns) to guess
-    the bins of the k-th key.  An unrepresentative sample (the columns it
-    reads hold only small values) and a gathered list that overflows one
-    wavefront's share (every large value in the first eighth of the row)
-    must both fall back to the exact three-pass path.  With the split
-    workspace the same rows overflow their chunk lists and fall back too."""
+    """Rows of more than 4096 candidates are sampled (256 of every 4096
+    columns) to set a threshold for the listing pass.  An unrepresentative
+    sample (the columns it reads hold only small values: the list has fewer
+    than k keys) and a list that overflows one wavefront's region (every
+    large value in the first eighth of the row) must both fall back to the
+    exact digit passes."""
     announce(f"select_topk sample misses / overflow ws={ws}")
     rng = np.random.default_rng(21)
     rows, M, k = 4, 65536, 2048
@@ -107,15 +128,15 @@ def test_select_topk_long_rows(ws):
 
 @pytest.mark.parametrize("k", [1, 100, 2048, 3000])
 def test_select_topk_split_rows(k):
-    """The split path: lengths around the chunk boundaries (chunks of 16384
-    columns, one chunk up to 16384, a last chunk of one column, 16 wider
-    chunks from 262144), values with many ties at the k-th key, signed
-    zeros and -inf.  k = 3000 expects too long a list, so those rows are
-    not split."""
+    """The split path (rows of more than 524288 columns with a workspace):
+    lengths around the chunk boundaries (chunks of 16384 columns, one chunk
+    up to 16384, a last chunk of one column, 16 wider chunks from 262144),
+    values with many ties at the k-th key, signed zeros and -inf.  k = 3000
+    expects too long a list, so those rows are not split."""
     announce(f"select_topk split rows k={k}")
     rng = np.random.default_rng(31 + k)
-    M = 300000
-    lens = [7681, 8192, 8193, 9000, 16385, 65536, 131072, 131073, 200000, 262145, 300000]
+    M = 600000
+    lens = [7681, 8192, 8193, 9000, 16385, 65536, 131072, 131073, 200000, 262145, 600000]
     rows = len(lens) + 2
     x = rng.standard_normal((rows, M)).astype(np.float32)
     x[1] = np.round(x[1] * 64) / 64                 # ties at the k-th key
@@ -228,8 +249,9 @@ def test_fused_topk_against_oracle(variant, next_n, ws):
 @pytest.mark.parametrize("variant", ["fp8", "fp4"])
 @pytest.mark.parametrize("next_n", [1, 2])
 def test_fused_topk_split_rows(variant, next_n):
-    """Rows too long for LDS (split over workgroups with the workspace) in
-    the fused step, whose candidate counts come from the schedule."""
+    """Rows of more than 4096 candidates (a workgroup each) beside shorter
+    rows (a wavefront each) in the fused step, whose candidate counts come
+    from the schedule."""
     announce(f"fused top-k split rows {variant} next_n={next_n}")
     ctx = np.array([0, 7700, 8193, 20000, 33000, 5000, 41000, 1], np.int64)
     mk = make_fp8 if variant == "fp8" else make_fp4

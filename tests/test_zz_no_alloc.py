@@ -52,12 +52,13 @@ def _check(x, n, k, label):
 
 def test_noalloc_matches_select_topk_on_two_calls():
     k = 2048
-    announce("select_topk_noalloc call 1: 40 rows x 40000")
-    assert pmqa.select_workspace_bytes(40, 40000, k) > 0    # the split path runs
-    x, n = _rows(90, 40, 40000, k)
+    announce("select_topk_noalloc call 1: 24 rows x 600000")
+    assert pmqa.select_workspace_bytes(24, 600000, k) > 0    # the split path runs
+    x, n = _rows(90, 24, 600000, k)
     _check(x, n, k, "call 1")
-    announce("select_topk_noalloc call 2: 9 rows x 20001")
-    x, n = _rows(91, 9, 20001, k)
+    announce("select_topk_noalloc call 2: 9 rows x 530001")
+    assert pmqa.select_workspace_bytes(9, 530001, k) > 0
+    x, n = _rows(91, 9, 530001, k)
     _check(x, n, k, "call 2")
 
 
