@@ -659,7 +659,7 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
 // A row whose sample has no finite range or whose bin b holds more than 64
 // keys is selected by 8-bit digits of its keys instead (four counting reads
 // and the write), the k-th key's equal keys taken by column.
-constexpr int32_t kWaveCols = 4096;  // rows selected by one wavefront, at most
+constexpr int32_t kWaveCols = 6144;  // rows selected by one wavefront, at most
 constexpr int kRing = 4;             // 16-byte reads in flight per lane
 
 struct WaveLds {
