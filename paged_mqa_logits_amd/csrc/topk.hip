@@ -13,7 +13,7 @@
 // zeros matter; elsewhere they are compared and binned as floats.  Three
 // ways to select a row, each exact:
 //
-//   * Rows of at most kWaveCols (4096) candidates: one wavefront per row,
+//   * Rows of at most kWaveCols (6144) candidates: one wavefront per row,
 //     eight (512 threads) or sixteen (1024) rows to a workgroup, no
 //     workgroup barrier.  The wavefront reads its row three times (the
 //     first read from HBM, the others mostly from the caches): a histogram

@@ -55,7 +55,7 @@ def test_select_topk_matches_oracle(pool, M, stride, k, ws):
 @pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("rows", [512, 513, 3000, 8192, 8193])
 def test_select_topk_many_rows(rows, ws):
-    """Rows of at most 4096 candidates are selected by one wavefront each,
+    """Rows of at most 6144 candidates are selected by one wavefront each,
     eight (or sixteen) to a workgroup: every row is selected exactly once
     however the rows fall into the groups, with many empty and equal
     lengths."""
@@ -81,11 +81,11 @@ def test_select_topk_many_wide_rows(ws):
     rng = np.random.default_rng(77)
     rows, M, k = 1500, 12000, 2048
     x = rng.standard_normal((rows, M)).astype(np.float32)
-    n = rng.integers(4097, M + 1, size=rows).astype(np.int32)
-    n[::5] = rng.integers(2049, 4097, size=len(n[::5]))
+    n = rng.integers(6145, M + 1, size=rows).astype(np.int32)
+    n[::5] = rng.integers(2049, 6145, size=len(n[::5]))
     n[::7] = rng.integers(0, 2049, size=len(n[::7]))
-    n[3::11] = 4096
-    n[4::11] = 4097
+    n[3::11] = 6144
+    n[4::11] = 6145
     idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
                                 select_workspace=ws)
     _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
@@ -93,7 +93,7 @@ def test_select_topk_many_wide_rows(ws):
 
 @pytest.mark.parametrize("ws", WS)
 def test_select_topk_long_rows_sample_misses_and_overflows(ws):
-    """Rows of more than 4096 candidates are sampled (256 of every 4096
+    """Rows of more than 6144 candidates are sampled (256 of every 4096
     columns) to set a threshold for the listing pass.  An unrepresentative
     sample (the columns it reads hold only small values: the list has fewer
     than k keys) and a list that overflows one wavefront's region (every
@@ -249,7 +249,7 @@ def test_fused_topk_against_oracle(variant, next_n, ws):
 @pytest.mark.parametrize("variant", ["fp8", "fp4"])
 @pytest.mark.parametrize("next_n", [1, 2])
 def test_fused_topk_split_rows(variant, next_n):
-    """Rows of more than 4096 candidates (a workgroup each) beside shorter
+    """Rows of more than 6144 candidates (a workgroup each) beside shorter
     rows (a wavefront each) in the fused step, whose candidate counts come
     from the schedule."""
     announce(f"fused top-k split rows {variant} next_n={next_n}")
