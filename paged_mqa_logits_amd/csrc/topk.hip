@@ -76,6 +76,7 @@ constexpr int kPlanRun = 256;            // the plan samples 256 of every 4096 c
 constexpr float kListFill = 0.8f;        // expected list at most this share of kListCap
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Larger value <-> larger key; -0 sorts just below +0.
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -547,36 +548,59 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
   v4f x[kListLoads];
 #pragma unroll
   for (int m = 0; m < kListLoads; ++m) x[m] = rload(rs_c, 256 * m, lane);
-  for (int32_t b0 = c0;; b0 += kListLoads * 256) {
+  // A tile's keys are listed only while the region has room for them and,
+  // past them, for a slot per lane that takes the stores of the lane's keys
+  // not listed (rewritten later, or never read), so that every store is
+  // unconditional; a tile without that room marks the region as overflowed
+  // (the row then takes the digit passes).
+  auto list_tile = [&](const v4f& v, int32_t t, const uint64_t (&ms)[4]) {
+    uint32_t tot = 0;
 #pragma unroll
-    for (int m = 0; m < kListLoads; ++m) {
-      // columns of the lane at or past c1 (the chunk's end) are not the row's
-      const int32_t lim = c1 - (b0 + 256 * m + 4 * lane);
-      bool sel[4];
-      uint64_t ms[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sel[e] = (x[m][e] >= T) & (e < lim);
-        ms[e] = __ballot(sel[e]);
-      }
+    for (int e = 0; e < 4; ++e) tot += (uint32_t)__builtin_popcountll(ms[e]);
+    if (mine + tot + 64u <= R) {
       uint32_t slot = mine;
 #pragma unroll
       for (int e = 0; e < 4; ++e) slot += lanes_below(ms[e]);
-      const uint32_t off = (uint32_t)(b0 + 256 * m + 4 * lane - c0);
+      const uint32_t spare = mine + tot + (uint32_t)lane;
+      const uint32_t off = (uint32_t)(t + 4 * lane - c0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (sel[e] & (slot < R)) {
-          lkey[slot] = x[m][e];
-          lcol[slot] = (uint16_t)(off + e);
-        }
-        slot += sel[e] ? 1u : 0u;
+        const bool in = __builtin_amdgcn_inverse_ballot_w64(ms[e]);
+        const uint32_t q = in ? slot : spare;
+        lkey[q] = v[e];
+        lcol[q] = (uint16_t)(off + e);
+        slot += in ? 1u : 0u;
       }
+      mine += tot;
+    } else {
+      mine = R + 1u;
+    }
+  };
+  // rounds of kListLoads whole tiles, then the chunk's last, partial round
+  // (the loop's last refills read past the chunk: zeros, no memory touched)
+  int32_t b0 = c0;
+  for (; b0 + kListLoads * 256 <= c1; b0 += kListLoads * 256) {  // uniform
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mine += (uint32_t)__builtin_popcountll(ms[e]);
+    for (int m = 0; m < kListLoads; ++m) {
+      uint64_t ms[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ms[e] = __builtin_amdgcn_ballot_w64(x[m][e] >= T);
+      list_tile(x[m], b0 + 256 * m, ms);
       x[m] = rload(rs_c, b0 - c0 + 256 * (m + kListLoads), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (b0 + kListLoads * 256 >= c1) break;  // one exit, at the end: every slot's wait is exact
+  }
+#pragma unroll
+  for (int m = 0; m < kListLoads; ++m) {
+    const int32_t t = b0 + 256 * m;
+    if (t < c1) {
+      // columns of the lane at or past c1 (the chunk's end) are not the row's
+      const int32_t lim = c1 - (t + 4 * lane);
+      uint64_t ms[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ms[e] = __builtin_amdgcn_ballot_w64((x[m][e] >= T) & (e < lim));
+      list_tile(x[m], t, ms);
+    }
   }
   if (lane == 0) f.wcnt[wave] = mine;
   __syncthreads();
@@ -654,16 +678,24 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
 //      wavefront's own histogram;
 //   2. the keys of the bin b of the k-th largest key (at most 64) listed with
 //      their columns, and the cut found from them;
-//   3. the selected columns written in column order, each lane's rank
-//      within the wavefront from ballots.
+//   3. the selected columns in column order, each lane's rank within the
+//      wavefront from ballots, staged in LDS and written in whole blocks.
 // A row whose sample has no finite range or whose bin b holds more than 64
 // keys is selected by 8-bit digits of its keys instead (four counting reads
 // and the write), the k-th key's equal keys taken by column.
 constexpr int32_t kWaveCols = 6144;  // rows selected by one wavefront, at most
 constexpr int kRing = 4;             // 16-byte reads in flight per lane
 
-struct WaveLds {
-  uint32_t hist[kFastBins + 4];  // [kFastBins]: columns out of range
+constexpr int kOutSlots = 512 + 64;  // staging slots: two blocks of 256, then one per lane
+
+struct alignas(16) WaveLds {
+  union {
+    uint32_t hist[kFastBins + 4];  // [kFastBins]: columns out of range
+    struct {
+      int32_t idx[kOutSlots];
+      float val[kOutSlots];
+    } out;  // the write's staging, once the histogram is no longer read
+  };
   uint32_t skey[kSmall];
   int32_t scol[kSmall];
 };
@@ -674,51 +706,124 @@ __device__ __forceinline__ v4f row_quad(rsrc_t rs, int32_t t, int lane) {
   return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 4 * t, 0));
 }
 
-// Calls f(first column of the lane's quad, values) for every tile of 256
-// columns of the row in order, kRing reads in flight: each slot of the ring
-// is refilled kRing tiles ahead right after its tile is used, and the loop
-// has one exit, at its end, so every wait is for the slot's own read.
+template <bool B>
+struct Whole {
+  static constexpr bool value = B;
+};
+
+// Calls f(first column of the lane's quad, values, Whole<w>) for every tile
+// of 256 columns of the row in order, kRing reads in flight: each slot of
+// the ring is refilled kRing tiles ahead right after its tile is used.  The
+// loop takes the rounds of kRing tiles whose columns are all the row's
+// (w true: no column needs a test); the row's last, partial round follows
+// it (w false), with no further reads (reads past the row return zeros
+// without touching memory, so the loop's last refills are harmless).
 template <class F>
 __device__ __forceinline__ void each_tile(rsrc_t rs, int32_t n, F&& f) {
   const int lane = threadIdx.x & 63;
   v4f x[kRing];
 #pragma unroll
   for (int m = 0; m < kRing; ++m) x[m] = row_quad(rs, 256 * m, lane);
-  for (int32_t t0 = 0;; t0 += kRing * 256) {
+  int32_t t0 = 0;
+  for (; t0 + kRing * 256 <= n; t0 += kRing * 256) {  // uniform
 #pragma unroll
     for (int m = 0; m < kRing; ++m) {
-      if (t0 + 256 * m < n) f(t0 + 256 * m + 4 * lane, x[m]);  // uniform
+      f(t0 + 256 * m + 4 * lane, x[m], Whole<true>{});
       x[m] = row_quad(rs, t0 + 256 * (m + kRing), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t0 + kRing * 256 >= n) break;
+  }
+#pragma unroll
+  for (int m = 0; m < kRing; ++m)
+    if (t0 + 256 * m < n) f(t0 + 256 * m + 4 * lane, x[m], Whole<false>{});
+}
+
+// The selection of a row leaves through LDS: output entry p goes to slot
+// p mod 512 (two blocks of 256), and a block, once whole, is written with
+// one 16-byte store per lane for the indices and one for the values (1 KB
+// of consecutive output per instruction).  Written where they are ranked,
+// the entries would go out as 4-byte stores scattered over partial lines:
+// 33.6 MB of output took 16.4 us that way on MI355X, 7.4 us in 16-byte
+// stores.  `vec`: both output rows are 16-byte aligned; else a block leaves
+// as 4-byte stores, 256 consecutive bytes per instruction.
+__device__ __forceinline__ void flush_block(const WaveLds& w, uint32_t j, uint32_t cnt,
+                                            int32_t* oi, float* ov, bool vec) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t s = (j & 1u) * 256u, p = 256u * j;
+  __builtin_amdgcn_wave_barrier();
+  if (vec & (cnt == 256u)) {
+    const v4i a = *reinterpret_cast<const v4i*>(w.out.idx + s + 4 * lane);
+    *reinterpret_cast<v4i*>(oi + p + 4 * lane) = a;
+    if (ov) {
+      const v4f v = *reinterpret_cast<const v4f*>(w.out.val + s + 4 * lane);
+      *reinterpret_cast<v4f*>(ov + p + 4 * lane) = v;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t e = 64u * m + (uint32_t)lane;
+      if (e < cnt) {
+        oi[p + e] = w.out.idx[s + e];
+        if (ov) ov[p + e] = w.out.val[s + e];
+      }
+    }
   }
 }
 
-// Writes the lane's selected columns of one quad (sel bit e: column i + e)
-// at their ranks: pos plus the selected columns of the lower lanes and of
-// the lane's own lower columns.  Returns the quad's selected count over the
-// wavefront.
-__device__ __forceinline__ uint32_t write_quad(const v4f& x, int32_t i, const bool (&sel)[4],
-                                               uint32_t pos, int32_t k, int32_t* oi, float* ov) {
-  uint64_t ms[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ms[e] = __ballot(sel[e]);
+// Stages the lane's selected columns of one quad (bit `lane` of ms[e]:
+// column i + e) at their ranks, pos plus the selected columns of the lower
+// lanes and of the lane's own lower columns, and writes out the block the
+// quad completes, if any (a quad adds at most 256 entries, so at most one).
+// Every lane stores all four columns, those not selected into the lane's
+// own slot past the blocks, so no store waits on a branch.  A row selects
+// exactly k columns (fewer or more only for a row holding NaN, whose
+// selection is unspecified: every store stays in the staging).  The
+// selection stays in wavefront masks (scalar registers) throughout; a
+// lane's bit is used as a condition directly (inverse ballot).
+__device__ __forceinline__ void stage_quad(WaveLds& w, const v4f& x, int32_t i,
+                                           const uint64_t (&ms)[4], uint32_t& pos, int32_t k,
+                                           int32_t* oi, float* ov, bool vec) {
+  const int lane = threadIdx.x & 63;
   uint32_t p = pos;
 #pragma unroll
   for (int e = 0; e < 4; ++e) p += lanes_below(ms[e]);
+  const uint32_t trash = 512u + (uint32_t)lane;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if (sel[e] & (p < (uint32_t)k)) {
-      oi[p] = i + e;
-      if (ov) ov[p] = x[e];
-    }
-    p += sel[e] ? 1u : 0u;
+    const bool in = __builtin_amdgcn_inverse_ballot_w64(ms[e]);
+    const uint32_t q = in ? (p & 511u) : trash;
+    w.out.idx[q] = i + e;
+    w.out.val[q] = x[e];
+    p += in ? 1u : 0u;
   }
   uint32_t tot = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) tot += (uint32_t)__builtin_popcountll(ms[e]);
-  return tot;
+  const uint32_t before = min(pos, (uint32_t)k) >> 8, after = min(pos + tot, (uint32_t)k) >> 8;
+  if (after != before) flush_block(w, before, 256u, oi, ov, vec);
+  pos += tot;
+}
+
+// Writes the last, partial block of a row of k selected entries.
+__device__ __forceinline__ void finish_rows(const WaveLds& w, int32_t k, int32_t* oi, float* ov,
+                                            bool vec) {
+  if (k & 255) flush_block(w, (uint32_t)k >> 8, (uint32_t)k & 255u, oi, ov, vec);
+}
+
+__device__ __forceinline__ bool aligned16(const int32_t* oi, const float* ov) {
+  return ((reinterpret_cast<uintptr_t>(oi) | reinterpret_cast<uintptr_t>(ov)) & 15u) == 0;
+}
+
+// The value of an order key (the inverse of order_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// A wavefront row's bins: value-linear over the sample's range like lin_bin,
+// as one fused multiply-add (x s - lo s), a clamp and a truncation: monotone
+// in x, like every step.
+__device__ __forceinline__ uint32_t fast_bin(float x, float s, float c) {
+  return (uint32_t)__builtin_amdgcn_fmed3f(__builtin_fmaf(x, s, c), 0.f, (float)(kFastBins - 1));
 }
 
 __device__ __forceinline__ bool wave_fast(WaveLds& w, const float* row, rsrc_t rs, int32_t n,
@@ -730,53 +835,89 @@ __device__ __forceinline__ bool wave_fast(WaveLds& w, const float* row, rsrc_t r
   const float lo = wave_min(sv), hi = wave_max(sv);
   const float s = (float)kFastBins / (hi - lo);
   if (!(hi > lo) || !(s > 0.f) || !__builtin_isfinite(s)) return false;
+  const float c = -lo * s;
   // 1. the histogram (columns past n go to the extra bin)
-  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+  each_tile(rs, n, [&](int32_t i, const v4f& x, auto whole) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      atomicAdd(&w.hist[i + e < n ? lin_bin(x[e], lo, s) : (uint32_t)kFastBins], 1u);
+    for (int e = 0; e < 4; ++e) {
+      uint32_t bin = fast_bin(x[e], s, c);
+      if (!decltype(whole)::value) bin = i + e < n ? bin : (uint32_t)kFastBins;
+      atomicAdd(&w.hist[bin], 1u);
+    }
   });
   uint32_t b, above, h;
   find_bin<>(w.hist, (uint32_t)k, b, above, h);
   if (h > kSmall) return false;
-  // 2. the keys of bin b, then the cut
+  // 2. the keys of bin b (a few tiles hold any), then the cut
   uint32_t listed = 0;
-  each_tile(rs, n, [&](int32_t i, const v4f& x) {
-    bool in[4];
-    uint64_t ms[4];
+  each_tile(rs, n, [&](int32_t i, const v4f& x, auto whole) {
+    uint64_t ms[4], any = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      in[e] = (i + e < n) & (lin_bin(x[e], lo, s) == b);
-      ms[e] = __ballot(in[e]);
+      bool in = fast_bin(x[e], s, c) == b;
+      if (!decltype(whole)::value) in = in & (i + e < n);
+      ms[e] = __builtin_amdgcn_ballot_w64(in);
+      any |= ms[e];
     }
-    uint32_t slot = listed;
+    if (any) {
+      uint32_t slot = listed;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) slot += lanes_below(ms[e]);
+      for (int e = 0; e < 4; ++e) slot += lanes_below(ms[e]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (in[e] & (slot < (uint32_t)kSmall)) {
-        w.skey[slot] = order_key(x[e]);
-        w.scol[slot] = i + e;
+      for (int e = 0; e < 4; ++e) {
+        const bool in = __builtin_amdgcn_inverse_ballot_w64(ms[e]);
+        if (in & (slot < (uint32_t)kSmall)) {
+          w.skey[slot] = order_key(x[e]);
+          w.scol[slot] = i + e;
+        }
+        slot += in ? 1u : 0u;
       }
-      slot += in[e] ? 1u : 0u;
-    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) listed += (uint32_t)__builtin_popcountll(ms[e]);
+      for (int e = 0; e < 4; ++e) listed += (uint32_t)__builtin_popcountll(ms[e]);
+    }
   });
   uint32_t kc, unused;
   int32_t cc;
   find_cut(w.skey, w.scol, h, (uint32_t)k - above, 0, kc, cc, unused);
-  // 3. the selection
+  // 3. the selection (exactly k columns): a key above the cut's, or equal
+  //    to it at a column <= cc.  Where the cut's value is a normal float
+  //    with a normal float just below it, a key is above the cut's exactly
+  //    when its value is above the cut value, and equal or above exactly
+  //    when above that lower float: one compare per column, against a
+  //    threshold chosen by the column.  Otherwise (zeros, whose keys differ
+  //    but whose values compare equal; denormals; infinities) the keys are
+  //    compared.
+  const bool vec = aligned16(oi, ov);
+  const float xc = key_value(kc);
+  const uint32_t xb = __float_as_uint(xc);
+  const uint32_t ex = (xb >> 23) & 0xFFu;
   uint32_t pos = 0;
-  each_tile(rs, n, [&](int32_t i, const v4f& x) {
-    bool sel[4];
+  if ((ex >= 2u) & (ex <= 254u)) {
+    const float xlo = __uint_as_float((xb & 0x80000000u) ? xb + 1u : xb - 1u);
+    each_tile(rs, n, [&](int32_t i, const v4f& x, auto whole) {
+      uint64_t ms[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = order_key(x[e]);
-      sel[e] = (i + e < n) & ((key > kc) | ((key == kc) & (i + e <= cc)));
-    }
-    pos += write_quad(x, i, sel, pos, k, oi, ov);
-  });
+      for (int e = 0; e < 4; ++e) {
+        bool sel = x[e] > (i + e <= cc ? xlo : xc);
+        if (!decltype(whole)::value) sel = sel & (i + e < n);
+        ms[e] = __builtin_amdgcn_ballot_w64(sel);
+      }
+      stage_quad(w, x, i, ms, pos, k, oi, ov, vec);
+    });
+  } else {
+    each_tile(rs, n, [&](int32_t i, const v4f& x, auto whole) {
+      uint64_t ms[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(x[e]);
+        bool sel = (key > kc) | ((key == kc) & (i + e <= cc));
+        if (!decltype(whole)::value) sel = sel & (i + e < n);
+        ms[e] = __builtin_amdgcn_ballot_w64(sel);
+      }
+      stage_quad(w, x, i, ms, pos, k, oi, ov, vec);
+    });
+  }
+  finish_rows(w, k, oi, ov, vec);
   return true;
 }
 
@@ -788,7 +929,7 @@ __device__ __forceinline__ void wave_radix(WaveLds& w, rsrc_t rs, int32_t n, int
   for (int d = 24; d >= 0; d -= 8) {
     const int lane = threadIdx.x & 63;
     for (int j = lane; j < 256; j += 64) w.hist[j] = 0u;
-    each_tile(rs, n, [&](int32_t i, const v4f& x) {
+    each_tile(rs, n, [&](int32_t i, const v4f& x, auto) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = order_key(x[e]);
@@ -801,9 +942,11 @@ __device__ __forceinline__ void wave_radix(WaveLds& w, rsrc_t rs, int32_t n, int
     pmask |= 0xFFu << d;
     krem -= above;
   }
-  // prefix is the k-th largest key; krem of its equal keys are taken
+  // prefix is the k-th largest key; krem of its equal keys are taken (k
+  // columns in all)
+  const bool vec = aligned16(oi, ov);
   uint32_t pos = 0, eq = 0;
-  each_tile(rs, n, [&](int32_t i, const v4f& x) {
+  each_tile(rs, n, [&](int32_t i, const v4f& x, auto) {
     bool isq[4];
     uint64_t mq[4];
 #pragma unroll
@@ -814,16 +957,18 @@ __device__ __forceinline__ void wave_radix(WaveLds& w, rsrc_t rs, int32_t n, int
     uint32_t r = eq;  // equal keys before this lane's first column
 #pragma unroll
     for (int e = 0; e < 4; ++e) r += lanes_below(mq[e]);
-    bool sel[4];
+    uint64_t ms[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sel[e] = ((i + e < n) & (order_key(x[e]) > prefix)) | (isq[e] & (r < krem));
+      ms[e] = __builtin_amdgcn_ballot_w64(((i + e < n) & (order_key(x[e]) > prefix)) |
+                                          (isq[e] & (r < krem)));
       r += isq[e] ? 1u : 0u;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) eq += (uint32_t)__builtin_popcountll(mq[e]);
-    pos += write_quad(x, i, sel, pos, k, oi, ov);
+    stage_quad(w, x, i, ms, pos, k, oi, ov, vec);
   });
+  finish_rows(w, k, oi, ov, vec);
 }
 
 // One row by one wavefront.
@@ -832,6 +977,7 @@ __device__ __forceinline__ void select_row_wave(WaveLds& w, const float* row, in
   const int lane = threadIdx.x & 63;
   if (n <= k) {  // every candidate is selected: 4 columns per lane, 4 reads in flight
     const float ninf = -__builtin_inff();
+    const bool vec = aligned16(oi, ov);
     for (int32_t i0 = 4 * lane; i0 < k; i0 += 4 * 256) {
       v4f x[4];
 #pragma unroll
@@ -840,15 +986,27 @@ __device__ __forceinline__ void select_row_wave(WaveLds& w, const float* row, in
         x[m] = i < n ? *reinterpret_cast<const v4f*>(row + i) : v4f{ninf, ninf, ninf, ninf};
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m) {
+        const int32_t i = i0 + 256 * m;
+        v4i a;
+        v4f v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int32_t c = i0 + 256 * m + e;
-          if (c < k) {
-            oi[c] = c < n ? c : -1;
-            if (ov) ov[c] = c < n ? x[m][e] : ninf;
-          }
+          a[e] = i + e < n ? i + e : -1;
+          v[e] = i + e < n ? x[m][e] : ninf;
         }
+        if (vec & (i + 3 < k)) {  // whole quads in 16-byte stores
+          *reinterpret_cast<v4i*>(oi + i) = a;
+          if (ov) *reinterpret_cast<v4f*>(ov + i) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i + e < k) {
+              oi[i + e] = a[e];
+              if (ov) ov[i + e] = v[e];
+            }
+        }
+      }
     }
     return;
   }

@@ -91,6 +91,30 @@ def test_select_topk_many_wide_rows(ws):
     _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+def test_select_topk_output_alignment(offset):
+    """Output rows are written in 16-byte stores only where both output rows
+    start on a 16-byte boundary; outputs given as views starting 1-3
+    elements into their storage take 4-byte stores, with the same result.
+    Rows of at most k, of a wavefront's and of a workgroup's lengths, with k
+    not a multiple of 256 (a partial last block)."""
+    announce(f"select_topk output offset {offset}")
+    rng = np.random.default_rng(300 + offset)
+    rows, M, k = 96, 9000, 2000
+    x = rng.standard_normal((rows, M)).astype(np.float32)
+    n = rng.integers(0, M + 1, size=rows).astype(np.int32)
+    n[:6] = [0, 1999, 2000, 2001, 6144, 6145]
+    idx_buf = torch.full((rows, k + 8), -7, dtype=torch.int32, device="cuda")
+    val_buf = torch.full((rows, k + 8), 7.0, dtype=torch.float32, device="cuda")
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                indices=idx_buf[:, offset:offset + k],
+                                values=val_buf[:, offset:offset + k], select_workspace=None)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+    ib, vb = idx_buf.cpu().numpy(), val_buf.cpu().numpy()
+    outside = np.r_[0:offset, offset + k:k + 8]    # columns of the storage outside the view
+    assert (ib[:, outside] == -7).all() and (vb[:, outside] == 7.0).all()
+
+
 @pytest.mark.parametrize("ws", WS)
 def test_select_topk_long_rows_sample_misses_and_overflows(ws):
     """Rows of more than 6144 candidates are sampled (256 of every 4096
