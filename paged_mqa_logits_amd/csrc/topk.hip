@@ -94,6 +94,45 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // given, else the fused indexer rule: min(causal limit, 256 c_b, max_ctx)
 // with c_b the row's unit count in the schedule (0 if the schedule header
 // does not describe this call).
+// Histogram adds of the digit passes, which count keys that may all be
+// equal (a row of -inf past a context, a crowded digit): 64 same-address
+// LDS atomics from one instruction are executed one after another, which
+// made such a row of 65536 columns take over a millisecond.  When every
+// lane of the wavefront adds to the first lane's bin (all four of a quad's
+// columns, for hist_add4), one atomic adds them all; otherwise each adds
+// its own.
+__device__ __forceinline__ bool first_lane() {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(__builtin_amdgcn_read_exec() >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)__builtin_amdgcn_read_exec(),
+                                                             0u)) == 0u;
+}
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
+  const uint64_t exec = __builtin_amdgcn_read_exec();
+  if (__builtin_amdgcn_ballot_w64(active & (bin == b0)) == exec) {  // uniform
+    if (first_lane()) atomicAdd(&hist[b0], (uint32_t)__builtin_popcountll(exec));
+  } else if (active) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+__device__ __forceinline__ void hist_add4(uint32_t* hist, const uint32_t (&bin)[4],
+                                          const bool (&active)[4]) {
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin[0]);
+  bool all = true;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) all = all & active[e] & (bin[e] == b0);
+  const uint64_t exec = __builtin_amdgcn_read_exec();
+  if (__builtin_amdgcn_ballot_w64(all) == exec) {  // uniform
+    if (first_lane()) atomicAdd(&hist[b0], 4u * (uint32_t)__builtin_popcountll(exec));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (active[e]) atomicAdd(&hist[bin[e]], 1u);
+  }
+}
+
 __device__ __forceinline__ int32_t row_candidates(int32_t r, int32_t max_ctx,
                                                   const int32_t* lengths, const int32_t* ctx,
                                                   const int32_t* sched, int32_t batch,
@@ -368,16 +407,15 @@ __device__ __forceinline__ v4f quad_at(const float* row, int32_t col, int32_t n)
   return v;
 }
 
-// Calls f(column, values) for every quad of a long row's sample: the first
-// kSampleRun columns of every kSampleStride.
-template <int kSelThreads, class F>
-__device__ __forceinline__ void each_sample_quad(const float* row, int32_t n, F&& f) {
-  constexpr int32_t kRunQuads = kSampleRun / 4;
-  const int32_t groups = (n + kSampleStride - 1) / kSampleStride;
-  for (int32_t t = threadIdx.x; t < groups * kRunQuads; t += kSelThreads) {
-    const int32_t col = kSampleStride * (t / kRunQuads) + 4 * (t % kRunQuads);
-    if (col < n) f(col, quad_at(row, col, n));
-  }
+// The sample of a long row (the listing path): G runs of 256 columns, one
+// per 4096 columns of the row up to two quads per thread (G at most
+// 2 kSelThreads / 64), run g starting at column g D, D = floor(n / G)
+// rounded down to a multiple of 4: runs at least 3072 columns apart for
+// rows of more than 6144, the last ending at most n - D + 256 < n.  Quad q
+// of the sample (of 64 G) is read by thread q mod kSelThreads.
+template <int kSelThreads>
+__device__ __forceinline__ int32_t sample_runs(int32_t n) {
+  return min((n + 4095) / 4096, 2 * kSelThreads / 64);
 }
 
 __device__ __forceinline__ uint32_t lin_bin(float x, float lo, float s) {
@@ -497,16 +535,28 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     f.hist2[j] = 0u;
   }
   if (tid == 0) f.scnt = 0u;
-  // 1. The sample's range, then its histogram.
+  // 1. The sample (held in registers: quads tid and tid + kSelThreads), its
+  //    range, then its histogram.  (Issuing the listing's first reads here
+  //    too, to arrive while the sample is counted, measured no faster: the
+  //    sample's own reads then took as much longer.)
+  const int32_t G = sample_runs<kSelThreads>(n), nq = 64 * G;
+  const int32_t D = __builtin_amdgcn_readfirstlane((n / G) & ~3);
+  const bool in0 = tid < nq, in1 = tid + kSelThreads < nq;
+  const int32_t q0 = in0 ? tid : 0, q1 = in1 ? tid + kSelThreads : 0;
+  const v4f s0 = *reinterpret_cast<const v4f*>(row + (q0 >> 6) * D + 4 * (q0 & 63));
+  const v4f s1 = *reinterpret_cast<const v4f*>(row + (q1 >> 6) * D + 4 * (q1 & 63));
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  each_sample_quad<kSelThreads>(row, n, [&](int32_t col, const v4f& x) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (__builtin_isfinite(x[e])) {
-        lo = fminf(lo, x[e]);
-        hi = fmaxf(hi, x[e]);
-      }
-  });
+  for (int e = 0; e < 4; ++e) {
+    if (in0 & __builtin_isfinite(s0[e])) {
+      lo = fminf(lo, s0[e]);
+      hi = fmaxf(hi, s0[e]);
+    }
+    if (in1 & __builtin_isfinite(s1[e])) {
+      lo = fminf(lo, s1[e]);
+      hi = fmaxf(hi, s1[e]);
+    }
+  }
   lo = wave_min(lo);
   hi = wave_max(hi);
   if (lane == 0) {
@@ -519,24 +569,24 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     lo = fminf(lo, f.wlo[w]);
     hi = fmaxf(hi, f.whi[w]);
   }
-  const float s = (float)kFastBins / (hi - lo);
+  const float s = (float)kFastBins * __builtin_amdgcn_rcpf(hi - lo);
   if (!(hi > lo) || !(s > 0.f) || !__builtin_isfinite(s)) {
     __syncthreads();
     return false;
   }
-  each_sample_quad<kSelThreads>(row, n, [&](int32_t col, const v4f& x) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (col + e < n) atomicAdd(&f.hist[lin_bin(x[e], lo, s)], 1u);
-  });
+  for (int e = 0; e < 4; ++e) {
+    if (in0) atomicAdd(&f.hist[lin_bin(s0[e], lo, s)], 1u);
+    if (in1) atomicAdd(&f.hist[lin_bin(s1[e], lo, s)], 1u);
+  }
   __syncthreads();
   // T: one bin below the sample key of rank ks + 4.5 sqrt(ks) + 4.5
-  const int32_t ns = sample_size<kSampleRun>(n);
+  const int32_t ns = 256 * G;
   const float ks = (float)k * (float)ns / (float)n;
   const uint32_t rs = (uint32_t)min((float)ns, ceilf(ks + 4.5f * sqrtf(ks) + 4.5f));
   uint32_t bs, a0, h0;
   find_bin<>(f.hist, rs, bs, a0, h0);
-  const float T = lo + ((float)bs - 1.f) / s;
+  const float T = lo + ((float)bs - 1.f) * ((hi - lo) * (1.f / (float)kFastBins));
   // 2. Every key >= T, in column order, into the wavefront's region: a
   //    ring of kListLoads tiles in flight, each slot refilled (kListLoads
   //    tiles ahead) as soon as it is used; reads past the chunk touch no
@@ -611,13 +661,25 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     total += f.wcnt[w];
     over = over || f.wcnt[w] > R;
   }
-  // 3. The k-th largest listed key: bins over [T, sample max].
-  const float s2 = hi > T ? (float)kFastBins / (hi - T) : 0.f;
+  // 3. The k-th largest listed key: bins over [T, sample max].  The
+  //    wavefront's listed keys and their bins stay in registers for the
+  //    rest of the row (all of the region's reads issued at once): no
+  //    dependent LDS reads per round of 64 keys.
+  const float s2 = hi > T ? (float)kFastBins * __builtin_amdgcn_rcpf(hi - T) : 0.f;
   if (over || total < (uint32_t)k || !(s2 > 0.f) || !__builtin_isfinite(s2)) {
     __syncthreads();
     return false;
   }
-  for (uint32_t j = lane; j < mine; j += 64) atomicAdd(&f.hist2[lin_bin(lkey[j], T, s2)], 1u);
+  constexpr int kT = (int)(R + 63) / 64;
+  float kv[kT];
+  uint32_t bn[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const bool in = 64u * t + lane < mine;
+    kv[t] = in ? lkey[64 * t + lane] : T;  // slots past `mine` hold no key
+    bn[t] = lin_bin(kv[t], T, s2);
+    if (in) atomicAdd(&f.hist2[bn[t]], 1u);
+  }
   __syncthreads();
   uint32_t b, above, h;
   find_bin<>(f.hist2, (uint32_t)k, b, above, h);
@@ -626,17 +688,15 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     return false;
   }
   uint32_t gt = 0;
-  for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
-    const uint32_t j = j0 + lane;
-    const bool in = j < mine;
-    const float x = in ? lkey[j] : 0.f;
-    const uint32_t bn = lin_bin(x, T, s2);
-    gt += (uint32_t)__builtin_popcountll(__ballot(in & (bn > b)));
-    if (in & (bn == b)) {
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const bool in = 64u * t + lane < mine;
+    gt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(in & (bn[t] > b)));
+    if (in & (bn[t] == b)) {
       const uint32_t slot = atomicAdd(&f.scnt, 1u);
       if (slot < (uint32_t)kSmall) {
-        f.skey[slot] = order_key(x);
-        f.scol[slot] = c0 + (int32_t)lcol[j];
+        f.skey[slot] = order_key(kv[t]);
+        f.scol[slot] = c0 + (int32_t)lcol[64 * t + lane];
       }
     }
   }
@@ -648,18 +708,20 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
 #pragma unroll
   for (int w = 0; w < W; ++w) pos += w < wave ? f.wcnt[w] : 0u;
   // 4. The selection, from the wavefront's region in order.
-  for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
-    const uint32_t j = j0 + lane;
-    const bool in = j < mine;
-    const float x = in ? lkey[j] : 0.f;
-    const int32_t col = c0 + (in ? (int32_t)lcol[j] : 0);
-    const uint32_t key = order_key(x);
-    const bool sel = in & ((key > kc) | ((key == kc) & (col <= cc)));
-    const uint64_t m = __ballot(sel);
+  int32_t col[kT];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) col[t] = c0 + (int32_t)lcol[64 * t + lane];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    if (64u * t >= mine) break;  // uniform
+    const bool in = 64u * t + lane < mine;
+    const uint32_t key = order_key(kv[t]);
+    const bool sel = in & ((key > kc) | ((key == kc) & (col[t] <= cc)));
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
     const uint32_t p = pos + lanes_below(m);
     if (sel & (p < (uint32_t)k)) {
-      oi[p] = col;
-      if (ov) ov[p] = x;
+      oi[p] = col[t];
+      if (ov) ov[p] = kv[t];
     }
     pos += (uint32_t)__builtin_popcountll(m);
   }
@@ -833,7 +895,7 @@ __device__ __forceinline__ bool wave_fast(WaveLds& w, const float* row, rsrc_t r
   const float sv = row[(int32_t)(((int64_t)lane * n) >> 6)];
   for (int j = lane; j <= kFastBins; j += 64) w.hist[j] = 0u;
   const float lo = wave_min(sv), hi = wave_max(sv);
-  const float s = (float)kFastBins / (hi - lo);
+  const float s = (float)kFastBins * __builtin_amdgcn_rcpf(hi - lo);
   if (!(hi > lo) || !(s > 0.f) || !__builtin_isfinite(s)) return false;
   const float c = -lo * s;
   // 1. the histogram (columns past n go to the extra bin)
@@ -930,11 +992,15 @@ __device__ __forceinline__ void wave_radix(WaveLds& w, rsrc_t rs, int32_t n, int
     const int lane = threadIdx.x & 63;
     for (int j = lane; j < 256; j += 64) w.hist[j] = 0u;
     each_tile(rs, n, [&](int32_t i, const v4f& x, auto) {
+      uint32_t bin[4];
+      bool act[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = order_key(x[e]);
-        if ((i + e < n) & ((key & pmask) == prefix)) atomicAdd(&w.hist[(key >> d) & 0xFFu], 1u);
+        bin[e] = (key >> d) & 0xFFu;
+        act[e] = (i + e < n) & ((key & pmask) == prefix);
       }
+      hist_add4(w.hist, bin, act);
     });
     uint32_t g, above, h;
     find_bin<256>(w.hist, krem, g, above, h);
@@ -1056,8 +1122,8 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
       __syncthreads();
       for (uint32_t c = tid; c < limit; c += kSelThreads) {
         const uint32_t key = ckey[c];
-        if (c % R < lds.cand_cnt[c / R] && (key & pmask) == prefix)
-          atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        hist_add(hist, (key >> shift) & dmask,
+                 (c % R < lds.cand_cnt[c / R]) & ((key & pmask) == prefix));
       }
       __syncthreads();
       choose_bin<kSelThreads>(lds, hist, (int)dmask + 1, krem);
@@ -1240,9 +1306,14 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
   __syncthreads();
   if (!staged) {
     for_each_sample<kSelThreads, kSampleRun>(row, lds, n, [&](int32_t col, const v4f& v) {
+      uint32_t bin[4];
+      bool act[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+      for (int e = 0; e < 4; ++e) {
+        bin[e] = order_key(v[e]) >> kTopShift;
+        act[e] = col + e < n;
+      }
+      hist_add4(lds.hist, bin, act);
     });
     __syncthreads();
     const int32_t ns = sample_size<kSampleRun>(n);
@@ -1272,16 +1343,18 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
           if (i + e < c1) lds.stage[i + e] = v[e];
       }
     }
+    uint32_t bin[4], fbin[4];
+    bool in[4], inw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (i + e < c1) {
-        const uint32_t key = order_key(v[e]);
-        const uint32_t bin = key >> kTopShift;
-        atomicAdd(&lds.hist[bin], 1u);
-        if (bin >= wlo && bin <= whi)
-          atomicAdd(&fine[(bin - wlo) * kBins2 + ((key >> (kTopShift - 8)) & 0xFFu)], 1u);
-      }
+      const uint32_t key = order_key(v[e]);
+      bin[e] = key >> kTopShift;
+      in[e] = i + e < c1;
+      fbin[e] = (bin[e] - wlo) * kBins2 + ((key >> (kTopShift - 8)) & 0xFFu);
+      inw[e] = in[e] & (bin[e] >= wlo) & (bin[e] <= whi);
     }
+    hist_add4(lds.hist, bin, in);
+    hist_add4(fine, fbin, inw);
   });
   __syncthreads();
   choose_bin<kSelThreads>(lds, lds.hist, kBins, (uint32_t)k);
@@ -1410,12 +1483,15 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
       if (tid < kBins2) lds.hist2[tid] = 0;
       __syncthreads();
       for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
+        uint32_t bin[4];
+        bool act[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = order_key(v[e]);
-          if (i + e < c1 && (key & pmask) == prefix)
-            atomicAdd(&lds.hist2[(key >> shift) & dmask], 1u);
+          bin[e] = (key >> shift) & dmask;
+          act[e] = (i + e < c1) & ((key & pmask) == prefix);
         }
+        hist_add4(lds.hist2, bin, act);
       });
       __syncthreads();
       choose_bin<kSelThreads>(lds, lds.hist2, (int)dmask + 1, krem);
@@ -1629,9 +1705,14 @@ void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
     if (tid < kBins2) lds.hist2[tid] = 0;
     __syncthreads();
     for_each_sample<kSelThreads, kPlanRun>(row, lds, n, [&](int32_t col, const v4f& v) {
+      uint32_t bin[4];
+      bool act[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < n) atomicAdd(&lds.hist[order_key(v[e]) >> kTopShift], 1u);
+      for (int e = 0; e < 4; ++e) {
+        bin[e] = order_key(v[e]) >> kTopShift;
+        act[e] = col + e < n;
+      }
+      hist_add4(lds.hist, bin, act);
     });
     __syncthreads();
     const int32_t ns = sample_size<kPlanRun>(n);
@@ -1643,12 +1724,15 @@ void select_plan_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
       const uint32_t b = lds.chosen[0], above = lds.chosen[1];
       __syncthreads();
       for_each_sample<kSelThreads, kPlanRun>(row, lds, n, [&](int32_t col, const v4f& v) {
+        uint32_t bin[4];
+        bool act[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = order_key(v[e]);
-          if (col + e < n && (key >> kTopShift) == b)
-            atomicAdd(&lds.hist2[(key >> (kTopShift - 8)) & 0xFFu], 1u);
+          bin[e] = (key >> (kTopShift - 8)) & 0xFFu;
+          act[e] = (col + e < n) & ((key >> kTopShift) == b);
         }
+        hist_add4(lds.hist2, bin, act);
       });
       __syncthreads();
       choose_bin<kSelThreads>(lds, lds.hist2, kBins2, want - above);

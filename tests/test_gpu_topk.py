@@ -91,6 +91,25 @@ def test_select_topk_many_wide_rows(ws):
     _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
 
 
+@pytest.mark.parametrize("ws", WS)
+def test_select_topk_rows_padded_with_neg_inf(ws):
+    """Candidates past a row's finite values are -inf (a length beyond the
+    context): rows of -inf only and rows with fewer than k finite values
+    take the digit passes, whose histograms then count tens of thousands
+    of equal keys; the -inf columns are taken in column order."""
+    announce(f"select_topk -inf padded rows ws={ws}")
+    rng = np.random.default_rng(41)
+    rows, M, k = 12, 65536, 2048
+    x = np.full((rows, M), -np.inf, np.float32)
+    finite = [0, 1000, 3000, 0, 1500, 5000, 0, 2047, 2048, 2049, 100, 60000]
+    for r, f in enumerate(finite):
+        x[r, :f] = rng.standard_normal(f).astype(np.float32)
+    n = np.array([M, M, M, 6144, 6144, 6144, 3000, M, M, M, 40000, M], np.int32)
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+
+
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
 def test_select_topk_output_alignment(offset):
     """Output rows are written in 16-byte stores only where both output rows
