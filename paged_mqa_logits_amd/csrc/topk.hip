@@ -642,11 +642,15 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
   }
 #pragma unroll
   for (int m = 0; m < kListLoads; ++m) {
-    const int32_t t = b0 + 256 * m;
-    if (t < c1) {
+    const int32_t t = b0 + 256 * m;  // uniform
+    uint64_t ms[4];
+    if (t + 256 <= c1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ms[e] = __builtin_amdgcn_ballot_w64(x[m][e] >= T);
+      list_tile(x[m], t, ms);
+    } else if (t < c1) {
       // columns of the lane at or past c1 (the chunk's end) are not the row's
       const int32_t lim = c1 - (t + 4 * lane);
-      uint64_t ms[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) ms[e] = __builtin_amdgcn_ballot_w64((x[m][e] >= T) & (e < lim));
       list_tile(x[m], t, ms);
@@ -671,15 +675,18 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     return false;
   }
   constexpr int kT = (int)(R + 63) / 64;
+  const uint32_t nt = (mine + 63) / 64;  // rounds of 64 keys the wavefront listed (uniform)
   float kv[kT];
   uint32_t bn[kT];
 #pragma unroll
-  for (int t = 0; t < kT; ++t) {
-    const bool in = 64u * t + lane < mine;
-    kv[t] = in ? lkey[64 * t + lane] : T;  // slots past `mine` hold no key
-    bn[t] = lin_bin(kv[t], T, s2);
-    if (in) atomicAdd(&f.hist2[bn[t]], 1u);
-  }
+  for (int t = 0; t < kT; ++t)
+    if (t < nt) kv[t] = 64u * t + lane < mine ? lkey[64 * t + lane] : T;  // slots past `mine` hold no key
+#pragma unroll
+  for (int t = 0; t < kT; ++t)
+    if (t < nt) {
+      bn[t] = lin_bin(kv[t], T, s2);
+      if (64u * t + lane < mine) atomicAdd(&f.hist2[bn[t]], 1u);
+    }
   __syncthreads();
   uint32_t b, above, h;
   find_bin<>(f.hist2, (uint32_t)k, b, above, h);
@@ -690,6 +697,7 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
   uint32_t gt = 0;
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
+    if (t >= nt) break;  // uniform
     const bool in = 64u * t + lane < mine;
     gt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(in & (bn[t] > b)));
     if (in & (bn[t] == b)) {
@@ -710,10 +718,11 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
   // 4. The selection, from the wavefront's region in order.
   int32_t col[kT];
 #pragma unroll
-  for (int t = 0; t < kT; ++t) col[t] = c0 + (int32_t)lcol[64 * t + lane];
+  for (int t = 0; t < kT; ++t)
+    if (t < nt) col[t] = c0 + (int32_t)lcol[64 * t + lane];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
-    if (64u * t >= mine) break;  // uniform
+    if (t >= nt) break;  // uniform
     const bool in = 64u * t + lane < mine;
     const uint32_t key = order_key(kv[t]);
     const bool sel = in & ((key > kc) | ((key == kc) & (col[t] <= cc)));
@@ -1627,6 +1636,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
     if (r >= rows) return;
     const int32_t n = cands(r);
     if (n > kWaveCols) return;  // a wide worker's
+    if (n > 4096) __builtin_amdgcn_s_setprio(1);  // see the long rows' priority below
     select_row_wave(smem.wv[wave], logits + r * ldo, n, k, out_idx + r * ldk,
                     out_val ? out_val + r * ldk : nullptr);
     return;
@@ -1634,6 +1644,13 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
   const int64_t r = g - groups;
   const int32_t n = cands(r);
   if (n <= kWaveCols) return;  // a group's
+  // The rows that end last take the SIMDs' issue slots first: the
+  // wavefronts of rows of more than 32768 candidates and of wavefront rows
+  // of more than 4096 run at instruction priority 1 (the kernel is bound by
+  // instruction issue; measured on MI355X, large_fp8: 29.1 -> 28.4 us per
+  // call; priority 2 for the longest rows starves the wavefront rows and
+  // costs 2-3 us).
+  if (n > 32768) __builtin_amdgcn_s_setprio(1);
   select_row_wg<kSelThreads>(smem.sel, smem.fast, logits + r * ldo, r, n, k, out_idx + r * ldk,
                              out_val ? out_val + r * ldk : nullptr, SplitWs{});
 }
