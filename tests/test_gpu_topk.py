@@ -92,6 +92,31 @@ def test_select_topk_many_wide_rows(ws):
 
 
 @pytest.mark.parametrize("ws", WS)
+@pytest.mark.parametrize("M,k", [(3000, 700), (3000, 2999), (20000, 2048), (20000, 9)])
+def test_select_topk_special_cut_values(M, k, ws):
+    """Rows whose k-th key lands on a special value: the write compares
+    values against the cut directly only for normal cut values with a
+    normal value just below them; zeros (-0 < +0), denormals, the smallest
+    normals and infinities take the key compare.  Values drawn from a pool
+    of such numbers, with many ties, at wavefront and workgroup lengths."""
+    announce(f"select_topk special cut values M={M} k={k} ws={ws}")
+    rng = np.random.default_rng(M + 7 * k)
+    tiny = np.float32(np.finfo(np.float32).tiny)          # smallest normal
+    den = np.float32(1e-40)                               # a denormal
+    sub = np.array([1], np.uint32).view(np.float32)[0]    # smallest denormal
+    pool = np.array([-np.inf, -1.0, -tiny, -den, -sub, -0.0, 0.0, sub, den, tiny,
+                     np.float32(2) * tiny, 1.0, np.inf], np.float32)
+    rows = 24
+    x = rng.choice(pool, size=(rows, M)).astype(np.float32)
+    x[1::3] = rng.choice(pool[3:10], size=(len(x[1::3]), M))  # cuts among zeros and denormals
+    n = rng.integers(k + 1, M + 1, size=rows).astype(np.int32)
+    n[0] = M
+    idx, val = pmqa.select_topk(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                                select_workspace=ws)
+    _check_rows(x, n, k, idx.cpu().numpy(), val.cpu().numpy())
+
+
+@pytest.mark.parametrize("ws", WS)
 def test_select_topk_rows_padded_with_neg_inf(ws):
     """Candidates past a row's finite values are -inf (a length beyond the
     context): rows of -inf only and rows with fewer than k finite values
