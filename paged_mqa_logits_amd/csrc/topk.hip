@@ -20,11 +20,13 @@
 //     of value-linear bins set from a 64-point sample of the row, then the
 //     keys of the bin holding the k-th largest key (at most 64), whose
 //     ranking gives the cut (the k-th selected key and column), then the
-//     selected columns written in column order.  Rows of at most k
-//     candidates are copied.  A row the bins do not settle is selected by
-//     8-bit digits of its keys (four counting reads) instead.
-//   * Longer rows: one workgroup per row.  A 1/16 sample of the row gives a
-//     threshold T below which the k-th largest key lies only with a 4.5-sigma
+//     selected columns written in column order, staged in LDS and stored
+//     in whole 1 KB blocks.  Rows of at most k candidates are copied.  A
+//     row the bins do not settle is selected by 8-bit digits of its keys
+//     (four counting reads) instead.
+//   * Longer rows: one workgroup per row.  A 1/16 sample of the row (held in
+//     registers) gives a threshold T below which the k-th largest key lies
+//     only with a 4.5-sigma
 //     miss of the sample; one pass lists every key >= T (about 1.4 k) in LDS
 //     in column order, and the k-th largest listed key, the cut and the
 //     selection come from the list.  A list with fewer than k keys or one
@@ -37,11 +39,19 @@
 //     chunk, and the selection works on the list (falling back as above when
 //     the list is not whole or too short).
 //
+// The kernel is bound by instruction issue, not by HBM: eight wavefronts
+// share a SIMD, and a row's latency is its per-tile instruction count times
+// its passes.  So the hot loops keep selections in wavefront masks (a
+// lane's bit used directly as a condition), test columns against the row's
+// end only in the last round of tiles, store unconditionally (a spare slot
+// per lane takes the columns not selected), and the rows that end last run
+// at a raised instruction priority.
+//
 // Measured on MI355X (2048 rows of lognormal lengths up to 65536, k = 2048):
-// the selection takes ~38 us, against ~59 us with one workgroup per row for
-// every row; the groups of wavefronts hold the short and middle rows with
-// little per-row overhead, while the long rows, a fifth of the rows but two
-// thirds of the columns, get a workgroup each.
+// the selection takes ~29 us per call, against ~59 us with one workgroup
+// per row for every row; the groups of wavefronts hold the short and middle
+// rows with little per-row overhead, while the long rows, a fifth of the
+// rows but two thirds of the columns, get a workgroup each.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
