@@ -486,6 +486,12 @@ def main():
                     lambda: pmqa.select_topk(out, lengths, K_TOP, indices=tk_idx, values=tk_val,
                                              select_workspace=None), args.steps), 2),
                 "select_workspace_mb": round(sel_bytes / 2**20, 1)}
+        # the selection's algorithmic bytes: every candidate logit read once
+        # (4 B) and k index + value pairs written per row (8 B each)
+        sel_alg = 4 * int(lengths.to(torch.int64).sum().item()) + 8 * K_TOP * B * NN
+        topk["select_algorithmic_bytes"] = sel_alg
+        topk["select_frac_of_8tbps"] = round(
+            sel_alg / (topk["select_single_kernel_us"] * 1e-6) / (HBM_PEAK_GBPS * 1e9), 4)
 
         # decode drift: every non-empty row grows by one token per step, so rows
         # cross 256-token boundaries as decoding goes on; the graph refreshes the
