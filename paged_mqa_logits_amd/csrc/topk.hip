@@ -584,10 +584,20 @@ __device__ __forceinline__ bool fast_list(FastLds<kSelThreads>& f, const float* 
     __syncthreads();
     return false;
   }
+  {
+    // values below the sample's finite range (a row of -inf past its
+    // context) all land in bin 0: a wavefront of them adds with one atomic
+    uint32_t b0[4], b1[4];
+    bool a0[4], a1[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (in0) atomicAdd(&f.hist[lin_bin(s0[e], lo, s)], 1u);
-    if (in1) atomicAdd(&f.hist[lin_bin(s1[e], lo, s)], 1u);
+    for (int e = 0; e < 4; ++e) {
+      b0[e] = lin_bin(s0[e], lo, s);
+      b1[e] = lin_bin(s1[e], lo, s);
+      a0[e] = in0;
+      a1[e] = in1;
+    }
+    hist_add4(f.hist, b0, a0);
+    hist_add4(f.hist, b1, a1);
   }
   __syncthreads();
   // T: one bin below the sample key of rank ks + 4.5 sqrt(ks) + 4.5
