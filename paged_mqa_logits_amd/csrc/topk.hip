@@ -1400,43 +1400,48 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
     choose_bin<kSelThreads>(lds, fine + (b1 - wlo) * kBins2, kBins2, krem);
     const uint32_t b2 = lds.chosen[0];
     uint32_t krem2 = krem - lds.chosen[1];
+    const uint32_t h2 = lds.chosen[2];
     __syncthreads();  // the gather below overwrites the window histograms
     constexpr int kShift2 = kTopShift - 8;
     uint32_t pmask2 = ~0u << kShift2, prefix2 = ((b1 << 8) | b2) << kShift2;
     const uint32_t R = (uint32_t)long_cap<kSelThreads>() / kSelWaves;
     uint32_t* ckey = lds.cand_long.key;
     int32_t* ccol = lds.cand_long.col;
-    uint32_t mine = 0;
-    for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
-      uint64_t bc[4];
+    // the histograms give the number of keys at or above prefix2 (k - krem2
+    // above it, h2 sharing it): a list that cannot hold them is not gathered
+    if ((uint32_t)k - krem2 + h2 <= R * kSelWaves) {  // uniform
+      uint32_t mine = 0;
+      for_each_tile(row, lds, false, c0, c1, [&](int32_t i, const v4f& v) {
+        uint64_t bc[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bc[e] = __ballot(i + e < c1 && order_key(v[e]) >= prefix2);
-      uint32_t slot = mine;
+        for (int e = 0; e < 4; ++e) bc[e] = __ballot(i + e < c1 && order_key(v[e]) >= prefix2);
+        uint32_t slot = mine;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
+        for (int e = 0; e < 4; ++e) slot += lanes_below(bc[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (((bc[e] >> lane) & 1u) && slot < R) {
-          ckey[wave * R + slot] = order_key(v[e]);
-          ccol[wave * R + slot] = i + e;
+        for (int e = 0; e < 4; ++e) {
+          if (((bc[e] >> lane) & 1u) && slot < R) {
+            ckey[wave * R + slot] = order_key(v[e]);
+            ccol[wave * R + slot] = i + e;
+          }
+          slot += (bc[e] >> lane) & 1u;
         }
-        slot += (bc[e] >> lane) & 1u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
+      });
+      if (lane == 0) lds.cand_cnt[wave] = mine;
+      __syncthreads();
+      bool overflow = false;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) overflow = overflow || lds.cand_cnt[w] > R;
+      if (!overflow) {
+        resolve(ckey, R, kShift2, pmask2, prefix2, krem2);
+        // prefix2 is the k-th largest key K; krem2 keys equal to it are taken
+        write_list(ckey, ccol, R, prefix2, krem2);
+        return;
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mine += __builtin_popcountll(bc[e]);
-    });
-    if (lane == 0) lds.cand_cnt[wave] = mine;
-    __syncthreads();
-    bool overflow = false;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) overflow = overflow || lds.cand_cnt[w] > R;
-    if (!overflow) {
-      resolve(ckey, R, kShift2, pmask2, prefix2, krem2);
-      // prefix2 is the k-th largest key K; krem2 keys equal to it are taken
-      write_list(ckey, ccol, R, prefix2, krem2);
-      return;
+      __syncthreads();  // the list is abandoned; the path below reuses its space
     }
-    __syncthreads();  // the list is abandoned; the path below reuses its space
   }
 
   // 2. The k-th largest key K (bits under pmask, the others free) and the
@@ -1505,11 +1510,14 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
     }
   }
   if (!counted && h1 != krem) {
-    // a crowded bin: further digits (8, 8, 5 bits) with passes over the row
+    // a crowded bin: the other 21 bits in two more passes over the row,
+    // digits of 11 and 10 bits counted in the first digit's histogram space
+    // (free now: the chosen bin is read, a staged row's gather is over)
+    static_assert(kTopShift <= 2 * kTopBits, "two digits of at most kTopBits bits");
     for (int top = kTopShift; top > 0;) {
-      const int shift = max(top - 8, 0);
+      const int shift = max(top - kTopBits, 0);
       const uint32_t dmask = (1u << (top - shift)) - 1u;
-      if (tid < kBins2) lds.hist2[tid] = 0;
+      for (int j = tid; j <= (int)dmask; j += kSelThreads) lds.hist[j] = 0;
       __syncthreads();
       for_each_tile(row, lds, staged, c0, c1, [&](int32_t i, const v4f& v) {
         uint32_t bin[4];
@@ -1520,10 +1528,10 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
           bin[e] = (key >> shift) & dmask;
           act[e] = (i + e < c1) & ((key & pmask) == prefix);
         }
-        hist_add4(lds.hist2, bin, act);
+        hist_add4(lds.hist, bin, act);
       });
       __syncthreads();
-      choose_bin<kSelThreads>(lds, lds.hist2, (int)dmask + 1, krem);
+      choose_bin<kSelThreads>(lds, lds.hist, (int)dmask + 1, krem);
       prefix |= lds.chosen[0] << shift;
       pmask |= dmask << shift;
       const uint32_t h = lds.chosen[2];
