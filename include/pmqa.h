@@ -272,7 +272,9 @@ pmqa_status_t paged_mqa_logits_fp4(const void* q, const void* q_scale, const voi
  *
  * One kernel (two more with the split workspace): rows of at most 6144
  * candidates are selected by one wavefront each, longer rows by one
- * workgroup each; no host synchronization; can be graph-captured.
+ * workgroup each (when every row gets a workgroup at once, at most two
+ * rows per compute unit, every row of more than k candidates gets one); no
+ * host synchronization; can be graph-captured.
  */
 pmqa_status_t select_topk(const float* logits, int64_t logits_stride, int32_t rows,
                           int32_t max_context_len, const int32_t* lengths, int32_t k,

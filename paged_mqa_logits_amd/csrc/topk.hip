@@ -13,7 +13,9 @@
 // zeros matter; elsewhere they are compared and binned as floats.  Three
 // ways to select a row, each exact:
 //
-//   * Rows of at most kWaveCols (6144) candidates: one wavefront per row,
+//   * Rows of at most kWaveCols (6144) candidates, when there are more rows
+//     than workgroups that fit on the chip at once (else only the rows
+//     copied whole): one wavefront per row,
 //     eight (512 threads) or sixteen (1024) rows to a workgroup, no
 //     workgroup barrier.  The wavefront reads its row three times (the
 //     first read from HBM, the others mostly from the caches): a histogram
@@ -1622,16 +1624,18 @@ __device__ __forceinline__ void select_row_wg(SelLds<kSelThreads>& lds, FastLds<
 }
 
 // Workgroups [0, groups) are groups: wavefront w of group g selects row
-// g kSelWaves + w, unless the row has more than kWaveCols candidates.
-// Workgroup groups + r then selects row r, the whole workgroup on it, if it
-// has more than kWaveCols candidates, and exits at once otherwise; the
+// g kSelWaves + w, unless the row has more than wave_cols candidates
+// (kWaveCols at most).  Workgroup groups + r then selects row r, the whole
+// workgroup on it, if it has more than wave_cols candidates, and exits at
+// once otherwise; the
 // dispatcher refills the freed slots with the next workgroups, so the wide
 // rows start within a few microseconds.  With a split workspace the grid is
 // one workgroup per row instead, in the order the plan kernel set.
 template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t rows,
-                        int32_t groups, int32_t max_ctx, const int32_t* __restrict__ lengths,
+                        int32_t groups, int32_t wave_cols, int32_t max_ctx,
+                        const int32_t* __restrict__ lengths,
                         const int32_t* __restrict__ ctx, const int32_t* __restrict__ sched,
                         int32_t batch, int32_t next_n, int32_t workers, int32_t k,
                         int32_t* __restrict__ out_idx, float* __restrict__ out_val, int64_t ldk,
@@ -1663,7 +1667,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
     const int64_t r = (int64_t)g * W + wave;
     if (r >= rows) return;
     const int32_t n = cands(r);
-    if (n > kWaveCols) return;  // a wide worker's
+    if (n > wave_cols) return;  // a wide worker's
     if (n > 4096) __builtin_amdgcn_s_setprio(1);  // see the long rows' priority below
     select_row_wave(smem.wv[wave], logits + r * ldo, n, k, out_idx + r * ldk,
                     out_val ? out_val + r * ldk : nullptr);
@@ -1671,7 +1675,7 @@ void select_topk_kernel(const float* __restrict__ logits, int64_t ldo, int32_t r
   }
   const int64_t r = g - groups;
   const int32_t n = cands(r);
-  if (n <= kWaveCols) return;  // a group's
+  if (n <= wave_cols) return;  // a group's
   // The rows that end last take the SIMDs' issue slots first: the
   // wavefronts of rows of more than 32768 candidates and of wavefront rows
   // of more than 4096 run at instruction priority 1 (the kernel is bound by
@@ -1966,17 +1970,24 @@ hipError_t launch_select_topk(const float* logits, int64_t ldo, int32_t rows, in
   const int64_t c = cus > 0 ? cus : 1;
   const bool big = (int64_t)rows <= 2 * c;  // 1024 threads: two workgroups per compute unit
   const int32_t waves = big ? 16 : 8;
+  // When every row gets a workgroup at once, a row is done sooner by its
+  // workgroup than by one wavefront: only rows that are copied whole (at
+  // most k candidates) stay with the groups.  Measured on MI355X, k = 2048:
+  // 64 rows of 6144 columns 24 -> 12 us, 64 rows of decode logits (lengths
+  // up to 65536) 19 -> 13 us, 256 rows 24 -> 19 us; a single row of 3000
+  // columns 8.5 -> 9.7 us.
+  const int32_t wave_cols = big ? min(k, kWaveCols) : kWaveCols;
   // without a split workspace: groups of wavefronts, then one workgroup per
   // row for the wide rows
   const int32_t groups = ws.map ? 0 : (int32_t)(((int64_t)rows + waves - 1) / waves);
   const dim3 grid(ws.map ? rows : groups + rows);
   if (big)
     hipLaunchKernelGGL(select_topk_kernel<1024>, grid, dim3(1024), 0, stream, logits, ldo, rows,
-                       groups, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
+                       groups, wave_cols, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
                        out_val, ldk, ws);
   else
     hipLaunchKernelGGL(select_topk_kernel<512>, grid, dim3(512), 0, stream, logits, ldo, rows,
-                       groups, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
+                       groups, wave_cols, max_ctx, lengths, ctx, sched, batch, next_n, workers, k, out_idx,
                        out_val, ldk, ws);
   return hipGetLastError();
 }
