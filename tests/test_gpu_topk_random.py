@@ -2,7 +2,9 @@
 widths, k, value distributions (normal, heavy ties, signed zeros, -inf
 padding, equal rows), lengths and output offsets drawn together, so that
 every selection path (copy, wavefront, workgroup listing, digit passes)
-meets shapes the targeted tests do not name."""
+meets shapes the targeted tests do not name.  Batches of at most two rows
+per compute unit give every row of more than k candidates a workgroup, so
+the wavefront path is drawn with more rows than that."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +16,14 @@ pytestmark = pytest.mark.gpu
 pmqa = pytest.importorskip("paged_mqa_logits_amd")
 
 
-def _case(seed):
+def _case(seed, many=False):
     rng = np.random.default_rng(seed)
-    rows = int(rng.integers(1, 160))
-    M = int(rng.choice([7, 300, 2100, 6143, 6145, 9000, 20000, 70000]))
+    if many:   # more rows than two per compute unit, mostly wavefront rows
+        rows = int(rng.integers(513, 1100))
+        M = int(rng.choice([300, 2100, 4097, 6143, 6144, 6145, 9000]))
+    else:
+        rows = int(rng.integers(1, 160))
+        M = int(rng.choice([7, 300, 2100, 6143, 6145, 9000, 20000, 70000]))
     k = int(rng.choice([1, 3, 64, 255, 256, 257, 1000, 2047, 2048, 3001]))
     kind = seed % 5
     if kind == 0:
@@ -42,11 +48,10 @@ def _case(seed):
     return x, n, k, off
 
 
-@pytest.mark.parametrize("seed", range(40))
-def test_select_topk_random_cases(seed):
-    x, n, k, off = _case(seed)
+def _run(seed, many):
+    x, n, k, off = _case(seed, many)
     rows, M = x.shape
-    announce(f"select_topk random seed {seed}: rows {rows} M {M} k {k} offset {off}")
+    announce(f"select_topk random seed {seed} many={many}: rows {rows} M {M} k {k} offset {off}")
     ib = torch.full((rows, k + 4), -7, dtype=torch.int32, device="cuda")
     vb = torch.full((rows, k + 4), 7.0, dtype=torch.float32, device="cuda")
     ld = (M + 3) // 4 * 4                            # row stride: a multiple of 4 columns
@@ -60,3 +65,13 @@ def test_select_topk_random_cases(seed):
         wi, wv = otk.select_topk(x[r], int(n[r]), k)
         assert np.array_equal(gi[r], wi), (seed, r)
         assert np.array_equal(gv[r].view(np.uint32), wv.view(np.uint32)), (seed, r)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_select_topk_random_cases(seed):
+    _run(seed, False)
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_select_topk_random_many_rows(seed):
+    _run(seed, True)
