@@ -247,7 +247,8 @@ def measure_ceiling(torch, kv_cache, page_bytes, pages, out, reps=10):
                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.pmqa_ceiling_fill.restype = ctypes.c_int
     lib.pmqa_ceiling_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
-                                      ctypes.c_int32, ctypes.c_void_p]
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -276,10 +277,17 @@ def measure_ceiling(torch, kv_cache, page_bytes, pages, out, reps=10):
             gather[f"{wps}w_{fl}p"] = round(g_bytes / (us * 1e-6) / 1e9, 1)
     f_bytes = out.numel() * 4
     fill = {}
-    for wps in (1, 2, 4, 8):
+    # (workgroups, threads, stores per round): 1-8 workgroups of 256 threads
+    # per compute unit, one store each per round; and fewer writers with 4
+    # stores each (one workgroup of 128 threads per 4 compute units is the
+    # shape of the library's flat -inf fill)
+    shapes = [(cus * w, 256, 1) for w in (1, 2, 4, 8)] + \
+             [(max(1, cus // 4), 128, 4), (max(1, 3 * cus // 8), 64, 4), (max(1, cus // 2), 64, 4)]
+    for blocks, threads, stores in shapes:
         us = per_launch_us(lambda: lib.pmqa_ceiling_fill(
-            ctypes.c_void_p(out.data_ptr()), out.numel(), float("-inf"), cus * wps, sp))
-        fill[f"{wps}w"] = round(f_bytes / (us * 1e-6) / 1e9, 1)
+            ctypes.c_void_p(out.data_ptr()), out.numel(), float("-inf"), blocks, threads, stores,
+            sp))
+        fill[f"{blocks}b_{threads}t_{stores}s"] = round(f_bytes / (us * 1e-6) / 1e9, 1)
     g_best = max(gather, key=gather.get)
     f_best = max(fill, key=fill.get)
     t = g_bytes / (gather[g_best] * 1e9) + f_bytes / (fill[f_best] * 1e9)

@@ -54,12 +54,13 @@ int pmqa_ceiling_gather(const void* kv_cache, int64_t num_pages, int32_t page_by
 /*
  * pmqa_ceiling_fill - write `value` over n_floats consecutive fp32 values
  * with 16-byte non-temporal stores, a grid-stride sweep of num_blocks
- * workgroups of PMQA_CEILING_THREADS threads.
+ * workgroups of `threads` threads (64, 128 or 256), each thread storing
+ * stores_per_round (1 or 4) quads a grid stride apart per round.
  *
  *   out       16-byte aligned; n_floats >= 4 and a multiple of 4.
  */
 int pmqa_ceiling_fill(float* out, int64_t n_floats, float value, int32_t num_blocks,
-                      hipStream_t stream);
+                      int32_t threads, int32_t stores_per_round, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -104,12 +104,18 @@ __global__ __launch_bounds__(kThreads) void ceiling_gather_kernel(
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// U = 16-byte stores per thread per round, a grid stride apart.
+template <int U>
 __global__ __launch_bounds__(kThreads) void ceiling_fill_kernel(v4f* __restrict__ out,
                                                                 int64_t n_quads, float value) {
   const v4f v = {value, value, value, value};
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_quads; i += stride)
-    __builtin_nontemporal_store(v, out + i);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (U - 1) * stride < n_quads; i += U * stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v, out + i + u * stride);
+  }
+  for (; i < n_quads; i += stride) __builtin_nontemporal_store(v, out + i);
 }
 
 template <int L>
@@ -148,9 +154,16 @@ extern "C" int pmqa_ceiling_gather(const void* kv_cache, int64_t num_pages, int3
 }
 
 extern "C" int pmqa_ceiling_fill(float* out, int64_t n_floats, float value, int32_t num_blocks,
-                                 hipStream_t stream) {
+                                 int32_t threads, int32_t stores_per_round, hipStream_t stream) {
   if (!out || n_floats < 4 || n_floats % 4 || num_blocks < 1 || (uintptr_t)out % 16) return 1;
-  hipLaunchKernelGGL(ceiling_fill_kernel, dim3(num_blocks), dim3(kThreads), 0, stream,
-                     reinterpret_cast<v4f*>(out), n_floats / 4, value);
+  if ((threads != 64 && threads != 128 && threads != 256) ||
+      (stores_per_round != 1 && stores_per_round != 4))
+    return 1;
+  if (stores_per_round == 1)
+    hipLaunchKernelGGL(ceiling_fill_kernel<1>, dim3(num_blocks), dim3(threads), 0, stream,
+                       reinterpret_cast<v4f*>(out), n_floats / 4, value);
+  else
+    hipLaunchKernelGGL(ceiling_fill_kernel<4>, dim3(num_blocks), dim3(threads), 0, stream,
+                       reinterpret_cast<v4f*>(out), n_floats / 4, value);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

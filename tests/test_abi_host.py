@@ -45,13 +45,16 @@ def test_ceiling_library_exports_its_header():
     p = ctypes.c_void_p
     lib.pmqa_ceiling_gather.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, ctypes.c_int64,
                                         ctypes.c_int32, ctypes.c_int32, p, p]
-    lib.pmqa_ceiling_fill.argtypes = [p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32, p]
+    lib.pmqa_ceiling_fill.argtypes = [p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, p]
     fake = 0x10000
     assert lib.pmqa_ceiling_gather(p(fake), 10, 8448, p(fake), 5, 4, 3, p(fake), p(0)) == 1
     assert lib.pmqa_ceiling_gather(p(fake), 10, 4000, p(fake), 5, 4, 2, p(fake), p(0)) == 1
     assert lib.pmqa_ceiling_gather(p(0), 10, 8448, p(fake), 5, 4, 2, p(fake), p(0)) == 1
-    assert lib.pmqa_ceiling_fill(p(fake), 6, 0.0, 4, p(0)) == 1
-    assert lib.pmqa_ceiling_fill(p(fake + 4), 8, 0.0, 4, p(0)) == 1
+    assert lib.pmqa_ceiling_fill(p(fake), 6, 0.0, 4, 256, 1, p(0)) == 1
+    assert lib.pmqa_ceiling_fill(p(fake + 4), 8, 0.0, 4, 256, 1, p(0)) == 1
+    assert lib.pmqa_ceiling_fill(p(fake), 8, 0.0, 4, 96, 1, p(0)) == 1      # threads
+    assert lib.pmqa_ceiling_fill(p(fake), 8, 0.0, 4, 128, 2, p(0)) == 1     # stores per round
 
 
 def test_schedule_bytes():
