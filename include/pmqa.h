@@ -82,9 +82,10 @@ typedef enum { PMQA_DTYPE_F32 = 0, PMQA_DTYPE_BF16 = 1 } pmqa_dtype_t;
 const char* pmqa_last_error(void);
 
 /* Persistent-grid size W of the fp8 logits kernel with next_n 1 and 64 heads
- * (the batch decode kernel) on `device`: compute units times its resident
- * workgroups per compute unit times 4 wavefronts per workgroup (one worker =
- * one wavefront).  Host-only query.  Returns -1 on failure (not a gfx950
+ * (the batch decode kernel) on `device`: three quarters of (compute units
+ * times its resident workgroups per compute unit), times 4 wavefronts per
+ * workgroup (one worker = one wavefront; the value of
+ * pmqa_default_num_workers for this kernel).  Host-only query.  Returns -1 on failure (not a gfx950
  * device, or a HIP error; pmqa_last_error() says which).
  *
  * Page: section 2 (a persistent grid whose work partition is computed per
@@ -94,10 +95,13 @@ const char* pmqa_last_error(void);
 int pmqa_num_workers(int device);
 
 /* Persistent-grid size for a logits kernel on `device`: compute units times
- * the kernel's resident workgroups per compute unit times 4 wavefronts per
- * workgroup (one worker = one wavefront).  The kernel, and so its
- * occupancy, depends on variant, next_n and num_heads (64, 32 or 16).
- * Host-only query; writes the count to *num_workers (host pointer). */
+ * the kernel's resident workgroups per compute unit, times 4 wavefronts per
+ * workgroup (one worker = one wavefront), except that the fp8 kernel with
+ * next_n 1 takes three quarters of those workgroups (it streams K faster
+ * with fewer readers; the next_n 2 and MXFP4 kernels, with twice the MFMA
+ * and epilogue work per byte, are fastest with all of them).  The kernel,
+ * and so its occupancy, depends on variant, next_n and num_heads (64, 32 or
+ * 16).  Host-only query; writes the count to *num_workers (host pointer). */
 pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next_n,
                                        int32_t num_heads, int32_t* num_workers);
 

@@ -273,7 +273,16 @@ pmqa_status_t pmqa_default_num_workers(int device, int32_t variant, int32_t next
   if (device != cur) hipSetDevice(cur);
   if (st != PMQA_OK) return st;
   if (blocks < 1) blocks = 1;
-  *num_workers = cus * blocks * pmqa::kWavesPerBlock;
+  int64_t groups = (int64_t)cus * blocks;
+  // The fp8 kernel with one query row per batch row streams K faster with
+  // fewer readers: three quarters of the workgroups that fit (measured on
+  // MI355X, B = 2048 decode: 768 workers 315 us per call, 1024 workers 323
+  // us; a plain gather of the same pages 6.89 against 6.82 TB/s).  Its
+  // next_n = 2 kernel and the MXFP4 kernel, with twice the MFMA and epilogue
+  // work per byte, are fastest with every workgroup (1024 workers 457 us
+  // against 768 workers 512 us for B = 256, next_n = 2).
+  if (variant == PMQA_VARIANT_FP8 && next_n == 1 && groups >= 8) groups = groups * 3 / 4;
+  *num_workers = (int32_t)(groups * pmqa::kWavesPerBlock);
   return ok();
 }
 
